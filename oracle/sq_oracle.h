@@ -1,0 +1,176 @@
+/*
+ * CPU ORACLE for the SmoothQuant W8A8 linear-layer path and the LLM.int8()
+ * mixed decomposition.  TEST INFRASTRUCTURE ONLY: only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  The product path
+ * never calls it, and it shares no code, header or table with the GPU path.
+ *
+ * Plain C11, built with -O2 -std=c11 -ffp-contract=off -fno-fast-math.
+ * Every floating-point step is one IEEE-754 binary32 operation with
+ * round-to-nearest-even unless a step says "double".  OpenMP is used only
+ * over independent output rows; each output element is computed by one
+ * thread in a fixed order, so results do not depend on the thread count.
+ *
+ * Pages cited (titles as printed on them):
+ *   [SQ-tutorial] "大语言模型量化技术（四）：SmoothQuant" (wangyu.me)
+ *   [SQ-practice] "大模型量化困局与SmoothQuant的破局思路" (lpnh.cn)
+ *   [SQ-ondevice] "如何通过 SmoothQuant 解决激活值离群点难题" (tbr8.org)
+ *   [SQ-wiki]     "SmoothQuant" encyclopedia entry (newton.com.tw)
+ *   [INT8-expl]   LLM.int8() explainer (xdnf.cn), "8 位推理为什么在 6.7B 处突然崩掉"
+ *
+ * Parity status of each function is stated beside it; "pinned" means a
+ * CPU test checks it against something other than itself (a printed worked
+ * example, a closed form, an invariant or a library routine).
+ *
+ * Layouts: row-major.  X is [M, K] (tokens x input channels), W is [N, K]
+ * (output x input channels, the nn.Linear layout), Y is [M, N].
+ * Element-type codes: 0 = fp32, 1 = fp16, 2 = bf16 (16-bit values are passed
+ * as their raw uint16 bit patterns).
+ */
+#ifndef SQ_ORACLE_H
+#define SQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+
+#define ORC_PER_TENSOR_STATIC 0
+#define ORC_PER_TOKEN_DYNAMIC 1
+
+/* Threads used by the parallel loops (OpenMP); n <= 0 leaves it unchanged. */
+int orc_set_num_threads(int n);
+
+/* Exact widening and round-to-nearest-even narrowing of 16-bit floats
+ * (IEEE-754 binary16; bfloat16 = upper half of binary32).  Pinned against
+ * numpy/torch conversions. */
+float orc_f16_to_f32(uint16_t h);
+float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_f16(float f);
+uint16_t orc_f32_to_bf16(float f);
+
+/* Round half to even, the rounding the quantizer uses. Pinned (ties). */
+float orc_round_half_even(float v);
+
+/* Per-channel abs-max: amax[c] = max_r |x[r, c]|; with accumulate != 0 the
+ * result is max(amax[c], that) (a running max over calibration batches).
+ * [SQ-tutorial] section 缩放因子, definition of x_j and w_j;
+ * [SQ-practice] §3.2 calibration code; [SQ-ondevice] §3 step 1 and 2.
+ * Pinned: numpy abs().max(axis=0). */
+void orc_absmax_cols(const void *x, int dt, int64_t rows, int64_t cols,
+                     int accumulate, float *amax);
+
+/* Smoothing factors.  s_j = max(xc^alpha / wc^(1-alpha), 1e-5) with
+ * xc = max(x_j, 1e-5), wc = max(w_j, 1e-5), the power and quotient in double
+ * and rounded once to fp32; inv_s_j = fl(1 / s_j).
+ * If static_scale != NULL: a = max(max_j fl(x_j * inv_s_j), 1e-8),
+ * static_scale[0] = fl(a / 127) (step), static_scale[1] = fl(127 / a).
+ * [SQ-tutorial] section 缩放因子 (equation for s_j and the three alpha cases);
+ * [SQ-practice] §2.1 formula and §3.2 clamps; [SQ-ondevice] §3 step 3.
+ * Pinned: worked example of [SQ-tutorial] 缩放的效果, alpha = 0 and 1 closed
+ * forms, alpha = 0.5 balance, smoothed-max closed form. */
+void orc_compute_scales(const float *act_amax, const float *w_amax, int64_t K,
+                        float alpha, float *s, float *inv_s, float *static_scale);
+
+/* Weight smoothing W'[n, k] = fl(W[n, k] * s[k]) (s == NULL: W' = W).
+ * [SQ-tutorial] SmoothQuant 的原理 (SW scales weight channel j by s_j);
+ * [SQ-ondevice] §3 step 4; [SQ-practice] §3.3 apply code.
+ * Pinned: column max of W' equals fl(s_j * w_j). */
+void orc_smooth_weights_f32(const void *w, int dt, int64_t N, int64_t K,
+                            const float *s, float *w_smoothed);
+
+/* Symmetric abs-max int8 quantization of each row of an fp32 matrix:
+ * a = max(max_k |v|, 1e-8); step = fl(a / 127); inv = fl(127 / a);
+ * q = clamp(round_half_even(fl(v * inv)), -127, 127).
+ * [INT8-expl] §2.1 quantize_absmax / quantize_vectorwise;
+ * [SQ-tutorial] 缩放的效果 (step = max / 127, round).
+ * Pinned: worked example, ties, clamp, zero row, error bound. */
+void orc_quantize_rows_f32(const float *v, int64_t rows, int64_t K, int8_t *q,
+                           float *step);
+
+/* a3: per-output-channel int8 weights of W' (above).  wq [N, K], w_scale [N]
+ * holds the per-row step.  [SQ-tutorial] 为什么激活不能用逐通道量化 (weights
+ * per output channel, dequant diag(delta_W) on the right). */
+void orc_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
+                        const float *s, int8_t *wq, float *w_scale);
+
+/* a4: xs = fl(X * inv_s) (inv_s == NULL: xs = X), then
+ *   mode PER_TOKEN_DYNAMIC: the row quantizer above, x_scale[M];
+ *   mode PER_TENSOR_STATIC: q = clamp(rhe(fl(xs * static_scale[1]))),
+ *                           x_scale[0] = static_scale[0].
+ * [SQ-tutorial] 为什么激活不能用逐通道量化 (per-tensor or per-token only);
+ * [SQ-practice] §3.3 (divide activations by s) and §7.3 (static vs dynamic);
+ * [SQ-ondevice] §3 (X_new = X / s). */
+void orc_quantize_act(const void *x, int dt, int64_t M, int64_t K,
+                      const float *inv_s, int mode, const float *static_scale,
+                      int8_t *xq, float *x_scale);
+
+/* a5: acc[m, n] = sum_k xq[m, k] * wq[n, k] (exact integer sum, checked in
+ * int64 and stored as int32); y = fl(fl((float)acc) * fl(dx_m * dw_n)) in
+ * fp32, then narrowed RNE to y_dt.  dx_m = x_scale[per_row ? m : 0].
+ * [SQ-tutorial] equation Y = diag(delta_X) X W diag(delta_W);
+ * [INT8-expl] §2.1 (int32 accumulation; outer-product c_x (x) c_w dequant).
+ * Pinned: int32 against numpy int64 matmul; unit scales give (float)acc;
+ * fp32 y within 1 ulp-ish of the double product.
+ * Returns the number of sums that did not fit int32 (0 expected). */
+int64_t orc_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M,
+                            int64_t N, int64_t K, const float *x_scale,
+                            int per_row, const float *w_scale, void *y,
+                            int y_dt, int32_t *acc_out);
+
+/* The same definition evaluated at sampled (row, col) pairs only; y and acc
+ * receive one element per pair (y in y_dt encoding). */
+void orc_gemm_i8_dequant_at(const int8_t *xq, const int8_t *wq, int64_t K,
+                            const float *x_scale, int per_row,
+                            const float *w_scale, int y_dt, const int64_t *rows,
+                            const int64_t *cols, int64_t n, void *y,
+                            int32_t *acc);
+
+/* LLM.int8() outlier columns: idx receives, ascending, every column j with
+ * some |X[m, j]| >= threshold (X fp16).  Returns |O|.
+ * [INT8-expl] §2.2 (columns whose magnitude exceeds the threshold form O)
+ * and §4.1 (any value above the threshold marks the dimension).
+ * Pinned: numpy brute force. */
+int64_t orc_outlier_columns(const uint16_t *x_f16, int64_t M, int64_t K,
+                            float threshold, int32_t *idx);
+
+/* LLM.int8() mixed matmul ([INT8-expl] §2.2 decomposition):
+ *  O from orc_outlier_columns; X~ = X with O columns zeroed; xq/x_scale =
+ *  per-token dynamic quantization of X~ (no smoothing); acc = xq . wq^T;
+ *  side[m, n] = sum over o in O ascending of fl(X[m,o] * W16[n,o]) in fp32
+ *  starting from 0; y = fl(fl((float)acc * fl(dx_m * dw_n)) + side), then
+ *  narrowed RNE to y_dt.  wq / w_scale are the weights' per-output-channel
+ *  int8 form (orc_smooth_weights with s == NULL, over all K).
+ *  Optional outputs (NULL to skip): acc_out [M,N], xq_out [M,K],
+ *  x_scale_out [M], idx_out [K] (first |O| used).  Returns |O|.
+ * Pinned: threshold +inf equals the plain vector-wise path; threshold tiny
+ * (every column in O) equals the fp32-accumulated fp16 product within its
+ * error bound. */
+int64_t orc_int8_mixed_matmul(const uint16_t *x_f16, int64_t M, int64_t K,
+                              const int8_t *wq, const float *w_scale,
+                              const uint16_t *w_f16, int64_t N, float threshold,
+                              void *y, int y_dt, int32_t *acc_out,
+                              int8_t *xq_out, float *x_scale_out,
+                              int32_t *idx_out);
+
+/* Mixed matmul at sampled (row, col) pairs, given the full O list and the
+ * quantized X~ (as produced by the call above on the same inputs). */
+void orc_int8_mixed_at(const uint16_t *x_f16, int64_t K, const int8_t *xq,
+                       const float *x_scale, const int8_t *wq,
+                       const float *w_scale, const uint16_t *w_f16,
+                       const int32_t *idx, int64_t n_idx, int y_dt,
+                       const int64_t *rows, const int64_t *cols, int64_t n,
+                       void *y, int32_t *acc);
+
+/* fp64 references ([SQ-tutorial] SmoothQuant 的原理: (XS^-1)(SW) = XW in
+ * the reals).  y64 [M, N] = X W^T in double; ys64 = (X diag(s)^-1)(diag(s) W)^T
+ * in double, with X/s and W*s each formed in double.  Pinned: the invariant
+ * ys64 = y64 to 1e-9 relative, and y64 against numpy float64 matmul. */
+void orc_matmul_f64(const void *x, int xdt, const void *w, int wdt, int64_t M,
+                    int64_t N, int64_t K, double *y64);
+void orc_smoothed_matmul_f64(const void *x, int xdt, const void *w, int wdt,
+                             const float *s, int64_t M, int64_t N, int64_t K,
+                             double *ys64);
+
+#endif
