@@ -1,0 +1,337 @@
+"""Benchmark of the W8A8 SmoothQuant linear-layer path on one MI355X.
+
+A step is one pass of the whole SmoothQuant path over one batch of the
+30B-class prefill layer (X fp16 [256, 7168] with 6 outlier channels x
+U(20,100), W fp16 [28672, 7168] ~ N(0, 0.025), alpha = 0.5, per-token int8 X,
+per-output-channel int8 W, bf16 out):
+
+  a1 abs-max of X   a1 abs-max of W   a2 smoothing factors
+  a3 W*s -> int8    a4 X/s -> int8    a5 int8 GEMM + dequant
+
+`value` is the step's int8 GEMM work (2*M*N*K ops) divided by the step time
+(TOPS), i.e. whole-path throughput.  The JSON line also carries the
+roofline of the step's dominant kernel, per-kernel times, and separately
+timed kernel-level figures: the prefill GEMM with cold weights (rotating
+copies larger than the 256 MB last-level cache), decode GEMMs at M = 1, 8,
+32 (HBM GB/s), activation quantization and abs-max on a 940 MB stream, the
+LLM.int8() mixed matmul and the hidden-1024 decoder GEMM set.  All inputs
+are seeded synthetic data, generated on the host and resident in HBM before
+any timed region.  `cpu_baseline` times the CPU oracle on a bounded slice
+of the same step on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5033.0      # MI355X dense int8 MFMA (256 CU x 2.4 GHz x 8192 ops/clk)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "W8A8 GEMM TOPS + % INT8 MFMA peak (prefill); decode GB/s as % of HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the step itself")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP event pairs on torch's current stream (the stream every call
+    below is launched on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_us(self, name):
+        ps = self.pairs[name]
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w8a8_post_quantization_amd as sq
+
+    L = sq.lib()
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def chk(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {L.sq_status_str(rc).decode()}")
+
+    # ------------------------------------------------------------ the step
+    M, N, K = 256, 28672, 7168
+    cfg = synth.prefill_30b(M, N, K)
+    X, W = T(cfg["X"]), T(cfg["W"])
+    del cfg
+    f32 = dict(dtype=torch.float32, device=dev)
+    xamax, wamax = torch.empty(K, **f32), torch.empty(K, **f32)
+    s, inv_s = torch.empty(K, **f32), torch.empty(K, **f32)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    ws = torch.empty(N, **f32)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(M, **f32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    kernels = [
+        ("a1_absmax_x", lambda: chk(L.sq_absmax_reduce(P(X), 1, M, K, 0, P(xamax), sp), "a1x")),
+        ("a1_absmax_w", lambda: chk(L.sq_absmax_reduce(P(W), 1, N, K, 0, P(wamax), sp), "a1w")),
+        ("a2_scales", lambda: chk(L.sq_compute_scales(P(xamax), P(wamax), K, 0.5, P(s), P(inv_s),
+                                                      None, sp), "a2")),
+        ("a3_smooth_weights", lambda: chk(L.sq_smooth_weights(P(W), 1, N, K, P(s), P(wq), P(ws),
+                                                              sp), "a3")),
+        ("a4_quantize_act", lambda: chk(L.sq_quantize_act(P(X), 1, M, K, P(inv_s), 1, None, P(xq),
+                                                          P(xs), sp), "a4")),
+        ("a5_gemm", lambda: chk(L.sq_gemm_i8_dequant(P(xq), P(wq), M, N, K, P(xs), 1, P(ws), P(y),
+                                                     2, None, sp), "a5")),
+    ]
+    bytes_per_call = {  # algorithmic HBM bytes of one launch
+        "a1_absmax_x": M * K * 2 + 4 * K,
+        "a1_absmax_w": N * K * 2 + 4 * K,
+        "a2_scales": 4 * 4 * K,
+        "a3_smooth_weights": N * K * 2 + N * K + 4 * K + 4 * N,
+        "a4_quantize_act": M * K * 2 + M * K + 4 * K + 4 * M,
+        "a5_gemm": M * K + N * K + M * N * 2 + 4 * M + 4 * N,
+    }
+    gemm_ops = 2.0 * M * N * K
+
+    for _ in range(args.warmup):
+        for _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        for name, fn in kernels:
+            tm.run(name, fn)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per_kernel = {}
+    for name, _ in kernels:
+        us = tm.avg_us(name)
+        per_kernel[name] = {"us": round(us, 2),
+                            "GBs": round(bytes_per_call[name] / us / 1e3, 1)}
+    per_kernel["a5_gemm"]["TOPS"] = round(gemm_ops / per_kernel["a5_gemm"]["us"] / 1e6, 1)
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
+    dom_us = per_kernel[dom]["us"]
+    if dom == "a5_gemm":
+        roof = {"bound": "mfma", "achieved": round(gemm_ops / dom_us / 1e6, 1),
+                "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_per_call[dom] / dom_us / 1e3, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    value = gemm_ops / (ms_per_step * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded SplitMix64 normals with planted outlier channels)",
+        "config": {"workload": "prefill_30b: SmoothQuant W8A8 linear layer, one full "
+                               "a1-a5 pass", "M": M, "N": N, "K": K, "alpha": 0.5,
+                   "x": "fp16, 6 channels x U(20,100)", "w": "fp16 N(0,0.025)",
+                   "act_quant": "per-token dynamic", "y": "bf16"},
+        "roofline": roof, "kernels": per_kernel, "wall_s_timed": round(wall, 3),
+    }
+    del X, W
+
+    if not args.no_extras:
+        out["extras"] = extras(torch, L, sp, T, chk)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _time_loop(torch, fns, iters):
+    """Average us per call of fns[i % len(fns)] over `iters` calls."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        fns[i % len(fns)]()
+    b.record()
+    torch.cuda.synchronize()
+    return 1000.0 * a.elapsed_time(b) / iters
+
+
+def extras(torch, L, sp, T, chk):
+    import synth
+
+    dev = torch.device("cuda:0")
+    P = lambda t: t.data_ptr()  # noqa: E731
+    res = {}
+
+    # Prefill GEMM with cold weights: 3 int8 weight copies (616 MB) rotate.
+    M, N, K = 256, 28672, 7168
+    g = torch.Generator(device=dev).manual_seed(1)
+    R = lambda *shape: torch.randint(-127, 128, shape, dtype=torch.int8, generator=g,  # noqa: E731
+                                     device=dev)
+    U = lambda n, scale: torch.rand(n, generator=g, device=dev) * scale + scale * 0.1  # noqa: E731
+    wqs = [R(N, K) for _ in range(3)]
+    ws, xq, xs = U(N, 1e-3), R(M, K), U(M, 1e-2)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fns = [lambda w=w: chk(L.sq_gemm_i8_dequant(P(xq), P(w), M, N, K, P(xs), 1, P(ws), P(y), 2,
+                                                None, sp), "gemm") for w in wqs]
+    us = _time_loop(torch, fns, 30)
+    tops = 2.0 * M * N * K / us / 1e6
+    res["gemm_prefill_cold"] = {"us": round(us, 2), "TOPS": round(tops, 1),
+                                "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    us_w = _time_loop(torch, fns[:1], 30)
+    res["gemm_prefill_warm"] = {"us": round(us_w, 2),
+                                "TOPS": round(2.0 * M * N * K / us_w / 1e6, 1)}
+    del wqs
+
+    # Decode: M in {1, 8, 32}, K = 8192, N = 28672, 3 rotating weight copies.
+    M, N, K = 32, 28672, 8192
+    wqs = [R(N, K) for _ in range(3)]
+    ws = U(N, 1e-3)
+    dec = {}
+    for m in (1, 8, 32):
+        xq, xs = R(m, K), U(m, 1e-2)
+        y = torch.empty((m, N), dtype=torch.float16, device=dev)
+        fns = [lambda w=w, xq=xq, xs=xs, y=y, m=m: chk(L.sq_gemm_i8_dequant(
+            P(xq), P(w), m, N, K, P(xs), 1, P(ws), P(y), 1, None, sp), "decode") for w in wqs]
+        us = _time_loop(torch, fns, 30)
+        b = N * K + m * K + m * N * 2 + 4 * m + 4 * N
+        dec[f"M{m}"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                        "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    res["decode"] = dec
+    del wqs
+
+    # Activation quantization and abs-max on a 940 MB stream (X fp16 [65536, 7168]).
+    M, K = 65536, 7168
+    Xs = torch.randn((M, K), dtype=torch.float16, generator=g, device=dev)
+    Xs[:, :6] *= 50.0
+    inv = U(K, 1.0)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    am = torch.empty(K, dtype=torch.float32, device=dev)
+    us = _time_loop(torch, [lambda: chk(L.sq_quantize_act(P(Xs), 1, M, K, P(inv), 1, None, P(xq),
+                                                          P(xs), sp), "quant")], 10)
+    b = M * K * 3 + 4 * K + 4 * M
+    res["quantize_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                              "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    us = _time_loop(torch, [lambda: chk(L.sq_absmax_reduce(P(Xs), 1, M, K, 0, P(am), sp),
+                                        "absmax")], 10)
+    b = M * K * 2 + 4 * K
+    res["absmax_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                            "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del Xs, xq
+
+    # LLM.int8() mixed matmul, X fp16 [2048, 4096] with 6 planted dims, tau = 6.
+    cfg = synth.llm_int8_2048()
+    Xm, Wm = T(cfg["X"]), T(cfg["W"])
+    M, K = Xm.shape
+    N = Wm.shape[0]
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    ws = torch.empty(N, dtype=torch.float32, device=dev)
+    chk(L.sq_smooth_weights(P(Wm), 1, N, K, None, P(wq), P(ws), sp), "wq")
+    need = L.sq_int8_mixed_matmul_workspace(M, K)
+    wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    us = _time_loop(torch, [lambda: chk(L.sq_int8_mixed_matmul(
+        P(Xm), M, K, P(wq), P(ws), P(Wm), N, 6.0, P(wsp), need, P(y), 1, P(cnt), sp), "mixed")],
+        20)
+    res["llm_int8_2048"] = {"us": round(us, 2), "n_outliers": int(cnt.item()),
+                            "TOPS": round(2.0 * M * N * K / us / 1e6, 1)}
+
+    # Hidden-1024 decoder GEMM set, M = 4096 (alpha only changes values).
+    M = 4096
+    total_us, total_ops, per = 0.0, 0.0, {}
+    for name, n, k in synth.DECODER_1024_WEIGHTS:
+        xq, wq, xs, ws = R(M, k), R(n, k), U(M, 1e-2), U(n, 1e-3)
+        y = torch.empty((M, n), dtype=torch.float16, device=dev)
+        us = _time_loop(torch, [lambda: chk(L.sq_gemm_i8_dequant(
+            P(xq), P(wq), M, n, k, P(xs), 1, P(ws), P(y), 1, None, sp), "dec1024")], 50)
+        ops = 2.0 * M * n * k
+        per[name] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 1)}
+        total_us += us
+        total_ops += ops
+    res["decoder_1024"] = {"per_gemm": per, "total_us": round(total_us, 2),
+                           "TOPS": round(total_ops / total_us / 1e6, 1),
+                           "frac_int8_peak": round(total_ops / total_us / 1e6 / PEAK_INT8_TOPS, 4)}
+    return res
+
+
+def cpu_baseline(seconds):
+    """The CPU oracle on a bounded slice of the step: the same a1-a5 pass over
+    all 256 tokens and K = 7168 but only the first n_cols output channels,
+    with n_cols sized for about `seconds` of work.  Reported in TOPS of the
+    slice's GEMM work over the slice's whole time."""
+    import oracle
+    import synth
+
+    threads = oracle.set_num_threads(0)
+    M, K = 256, 7168
+
+    def run(ncols):
+        X, W, _ = synth.linear_layer(2, M, ncols, K, 6, 20.0, 100.0, 0.025)
+        t0 = time.perf_counter()
+        xa = oracle.absmax_cols(X)
+        wa = oracle.absmax_cols(W)
+        s_, inv_ = oracle.compute_scales(xa, wa, 0.5)
+        wq_, ws_ = oracle.smooth_weights(W, s_)
+        xq_, xs_ = oracle.quantize_act(X, inv_, oracle.PER_TOKEN_DYNAMIC)
+        oracle.gemm_i8_dequant(xq_, wq_, xs_, ws_, y_dt=oracle.BF16, want_acc=False)
+        return time.perf_counter() - t0
+
+    n = 64
+    t = run(n)
+    n = int(max(64, min(28672, n * seconds / max(t, 1e-3))))
+    t = run(n)
+    ops = 2.0 * M * n * K
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"full a1-a5 pass on X [256,7168] and the first {n} of 28672 output "
+                      f"channels of W ({t:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

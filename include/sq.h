@@ -1,0 +1,182 @@
+/*
+ * sq.h - C ABI of the MI355X (gfx950) W8A8 SmoothQuant linear-layer library.
+ *
+ * The library implements, as hand-written HIP kernels, the per-layer path of
+ * SmoothQuant W8A8 post-training quantization and LLM.int8()'s mixed
+ * decomposition.  Pages defining each operation (titles as printed):
+ *   [SQ-tutorial] "大语言模型量化技术（四）：SmoothQuant" (wangyu.me)
+ *   [SQ-practice] "大模型量化困局与SmoothQuant的破局思路" (lpnh.cn)
+ *   [SQ-ondevice] "如何通过 SmoothQuant 解决激活值离群点难题" (tbr8.org)
+ *   [INT8-expl]   LLM.int8() explainer (xdnf.cn)
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller (allocated with
+ *    hipMalloc or by a framework); the library never allocates, frees or
+ *    keeps them.  Tensors are dense and row-major.
+ *  - Layouts: X is [M, K] (tokens x input channels, K contiguous), W is
+ *    [N, K] (output x input channels, the nn.Linear layout), Y is [M, N].
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; the library never synchronizes, so results are
+ *    ready once the stream is.  Calls that share output buffers must be
+ *    ordered by the caller.
+ *  - Every call returns an sq_status.  Argument errors are found on the host
+ *    before anything is enqueued and leave all outputs untouched.  A failed
+ *    launch returns SQ_ERR_HIP (hipGetLastError after the launch).
+ *  - Sizes are int64_t; 0 rows/tokens/outputs is allowed and enqueues
+ *    nothing (except where stated).  Row strides must be multiples of 16
+ *    bytes and int8 / 16-bit / fp32 tensor pointers 16-byte aligned, so the
+ *    kernels can move 16-byte vectors: K % 16 == 0 for int8 operands,
+ *    cols % 8 == 0 (16-bit) or cols % 4 == 0 (fp32) for reductions.
+ *  - Floating point: fp32 arithmetic, IEEE round-to-nearest-even, no
+ *    contraction of a*b+c into fma, denormals kept.  Inputs must be finite.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    SQ_ERR_SHAPE = 2,       /* negative size or unsupported divisibility */
+    SQ_ERR_DTYPE = 3,       /* element type not allowed for this argument */
+    SQ_ERR_ALIGN = 4,       /* pointer not 16-byte aligned */
+    SQ_ERR_ARG = 5,         /* alpha outside [0,1], threshold <= 0 or NaN, bad mode */
+    SQ_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+    SQ_ERR_UNSUPPORTED = 7, /* combination not implemented */
+    SQ_ERR_HIP = 8          /* the HIP runtime reported an error */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
+
+typedef enum { SQ_PER_TENSOR_STATIC = 0, SQ_PER_TOKEN_DYNAMIC = 1 } sq_qmode;
+
+/* Human-readable name of a status code (static string). */
+const char *sq_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int sq_version(void);
+
+/*
+ * a1 - per-channel abs-max (calibration statistics).
+ * [SQ-tutorial] 缩放因子: x_j = max_i |X_ij| (activations, over all tokens) and
+ * w_j = max over output channels of |W| in input channel j; [SQ-practice] §3.2
+ * and [SQ-ondevice] §3 compute both as column maxima.
+ *   x        [rows, cols] of dt (SQ_F32, SQ_F16 or SQ_BF16)
+ *   amax_out [cols] fp32: amax_out[c] = max_r |x[r, c]|.  With accumulate != 0
+ *            the result is max(previous amax_out[c], that) - a running max over
+ *            calibration batches; amax_out must then hold non-negative values.
+ *            rows == 0 gives 0 (or leaves the running max unchanged).
+ * Exact (a max of magnitudes has no rounding).  cols*size(dt) % 16 == 0.
+ */
+int sq_absmax_reduce(const void *x, int dt, int64_t rows, int64_t cols,
+                     int accumulate, float *amax_out, void *stream);
+
+/*
+ * a2 - smoothing factors.  [SQ-tutorial] 缩放因子, s_j = x_j^alpha / w_j^(1-alpha);
+ * clamps from [SQ-practice] §3.2.
+ *   act_amax, w_amax [K] fp32 (from a1)
+ *   s, inv_s         [K] fp32 out: xc = max(x_j, 1e-5), wc = max(w_j, 1e-5),
+ *                    s_j = max(xc^alpha / wc^(1-alpha), 1e-5) (powers and
+ *                    quotient in double, rounded once), inv_s_j = fl(1 / s_j).
+ *   static_scale     [2] fp32 out or NULL: the per-tensor static activation
+ *                    step {step, 1/step}: a = max(max_j fl(x_j * inv_s_j), 1e-8),
+ *                    step = fl(a / 127), inv = fl(127 / a).  Since rounding is
+ *                    monotone, a is the max of |fl(X * inv_s)| over the
+ *                    calibration data.
+ *   alpha in [0, 1].
+ */
+int sq_compute_scales(const float *act_amax, const float *w_amax, int64_t K,
+                      float alpha, float *s, float *inv_s, float *static_scale,
+                      void *stream);
+
+/*
+ * a3 - weight smoothing + per-output-channel int8.  [SQ-tutorial]
+ * SmoothQuant 的原理 (SW: weight input channel j times s_j) and
+ * 为什么激活不能用逐通道量化 (weights quantized per output channel);
+ * quantizer of [INT8-expl] §2.1 (scale 127/max, round, clip to +-127).
+ *   w       [N, K] of dt
+ *   s       [K] fp32, or NULL for s = 1 (plain per-channel quantization)
+ *   wq      [N, K] int8 out: w' = fl(W * s); a_n = max(max_k |w'|, 1e-8);
+ *           q = clamp(round_half_even(fl(w' * fl(127 / a_n))), -127, 127)
+ *   w_scale [N] fp32 out: fl(a_n / 127)
+ * K % 16 == 0.
+ */
+int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
+                      const float *s, int8_t *wq, float *w_scale, void *stream);
+
+/*
+ * a4 - fused smoothing and activation int8 quantization.  xs = fl(X * inv_s)
+ * ([SQ-ondevice] §3: X / s at inference; [SQ-practice] §3.3), then
+ *   SQ_PER_TOKEN_DYNAMIC: per row a = max(max_k |xs|, 1e-8),
+ *       x_scale[m] = fl(a / 127), q = clamp(rhe(fl(xs * fl(127 / a))), +-127)
+ *   SQ_PER_TENSOR_STATIC: q = clamp(rhe(fl(xs * static_scale[1])), +-127),
+ *       x_scale[0] = static_scale[0]
+ * ([SQ-tutorial] 为什么激活不能用逐通道量化: per-tensor or per-token only).
+ *   x            [M, K] of dt
+ *   inv_s        [K] fp32 or NULL (no smoothing, e.g. folded upstream)
+ *   static_scale [2] fp32 {step, 1/step} (static mode only, else ignored)
+ *   xq           [M, K] int8 out; x_scale [M] (dynamic) or [1] (static) out
+ * K % 16 == 0.
+ */
+int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
+                    const float *inv_s, int mode, const float *static_scale,
+                    int8_t *xq, float *x_scale, void *stream);
+
+/*
+ * a5 - int8 x int8 -> int32 GEMM with the outer-product dequant epilogue.
+ * [SQ-tutorial] Y = diag(delta_X) X_int8 W_int8 diag(delta_W);
+ * [INT8-expl] §2.1 (int32 accumulation, c_x (x) c_w).
+ *   xq [M, K] int8, wq [N, K] int8
+ *   x_scale: [M] fp32 if x_scale_per_row != 0, else [1] (per-tensor)
+ *   w_scale: [N] fp32
+ *   y  [M, N] of y_dt out: acc = sum_k xq[m,k] * wq[n,k] (exact int32),
+ *      y = fl(fl((float)acc) * fl(x_scale[m] * w_scale[n])) narrowed RNE.
+ *   acc_out [M, N] int32 out or NULL (the integer sums, for checking).
+ * K % 16 == 0; |acc| must fit int32 (holds for K <= 133143).  M <= 32 uses
+ * the skinny (decode) kernel, larger M the tiled MFMA kernel; both give the
+ * same bits.
+ */
+int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M,
+                       int64_t N, int64_t K, const float *x_scale,
+                       int x_scale_per_row, const float *w_scale, void *y,
+                       int y_dt, int32_t *acc_out, void *stream);
+
+/*
+ * a6 - LLM.int8() mixed-precision matmul ([INT8-expl] §2.2 decomposition;
+ * §4.1: a dimension is an outlier when any value reaches the threshold).
+ *   x         [M, K] fp16 activations
+ *   wq, w_scale  [N, K] int8 and [N] fp32: the weights' per-output-channel
+ *             int8 form over ALL K (sq_smooth_weights with s = NULL)
+ *   w_f16     [N, K] fp16 original weights (read only in outlier columns)
+ *   threshold > 0 (may be +inf: no outliers)
+ *   y         [M, N] of y_dt out:
+ *     O = ascending { j : some |x[m, j]| >= threshold };
+ *     X~ = x with the O columns zeroed, quantized per token (a4 dynamic,
+ *     no smoothing); acc = X~q . wq^T;
+ *     side = sum over o in O ascending of fl(x[m,o] * w[n,o]) in fp32 from 0;
+ *     y = fl(fl((float)acc * fl(dx_m * dw_n)) + side), narrowed RNE.
+ *   n_outliers_out  device int32 out or NULL: |O|.
+ *   workspace       device memory of at least
+ *                   sq_int8_mixed_matmul_workspace(M, K) bytes, 256-byte
+ *                   aligned; it holds X~q, the row steps, the column mask
+ *                   and the O list.  Contents on return are unspecified.
+ * K % 16 == 0.
+ */
+size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K);
+int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                         const float *w_scale, const void *w_f16, int64_t N,
+                         float threshold, void *workspace,
+                         size_t workspace_bytes, void *y, int y_dt,
+                         int32_t *n_outliers_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

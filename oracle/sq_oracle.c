@@ -118,15 +118,24 @@ static int8_t clamp_i8(float r) {
 
 void orc_absmax_cols(const void *x, int dt, int64_t rows, int64_t cols,
                      int accumulate, float *amax) {
+    /* amax[c] = max over rows of |x[r, c]|, rows visited in order for each
+     * column; threads own disjoint column ranges. */
+    const int64_t chunk = 256;
 #pragma omp parallel for schedule(static)
-    for (int64_t c = 0; c < cols; ++c) {
-        float m = 0.0f;
-        for (int64_t r = 0; r < rows; ++r) {
-            float a = fabsf(load_elem(x, dt, r * cols + c));
-            if (a > m) m = a;
+    for (int64_t c0 = 0; c0 < cols; c0 += chunk) {
+        const int64_t c1 = c0 + chunk < cols ? c0 + chunk : cols;
+        float m[256];
+        for (int64_t c = c0; c < c1; ++c) m[c - c0] = 0.0f;
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t c = c0; c < c1; ++c) {
+                float a = fabsf(load_elem(x, dt, r * cols + c));
+                if (a > m[c - c0]) m[c - c0] = a;
+            }
+        for (int64_t c = c0; c < c1; ++c) {
+            float v = m[c - c0];
+            if (accumulate && amax[c] > v) v = amax[c];
+            amax[c] = v;
         }
-        if (accumulate && amax[c] > m) m = amax[c];
-        amax[c] = m;
     }
 }
 

@@ -1,0 +1,117 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/sq.h declares, and rejects bad arguments on the host before any
+launch (so every error path is testable here).  No kernel is launched."""
+import ctypes
+import os
+
+import pytest
+
+import w8a8_post_quantization_amd as sq
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sq.LIB_PATH),
+                                reason="libsq.so not built (run __graft_entry__.build())")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ARG, WORKSPACE, UNSUP, HIP = range(9)
+FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced on these paths
+
+
+def test_exports_every_declared_symbol():
+    L = sq.lib()
+    declared = sq.header_functions()
+    assert len(declared) == 9
+    for name in declared:
+        assert hasattr(L, name), name
+        assert name in sq.SIGNATURES, name
+    assert L.sq_version() == 100
+
+
+def test_status_strings():
+    L = sq.lib()
+    for code in range(9):
+        assert L.sq_status_str(code).decode().startswith("SQ_")
+    assert b"unknown" in L.sq_status_str(42)
+
+
+def test_absmax_validation():
+    L = sq.lib()
+    assert L.sq_absmax_reduce(FAKE, 7, 4, 16, 0, FAKE, None) == DTYPE
+    assert L.sq_absmax_reduce(FAKE, sq.SQ_F16, -1, 16, 0, FAKE, None) == SHAPE
+    assert L.sq_absmax_reduce(FAKE, sq.SQ_F16, 4, 12, 0, FAKE, None) == SHAPE   # 24 B rows
+    assert L.sq_absmax_reduce(FAKE, sq.SQ_F32, 4, 6, 0, FAKE, None) == SHAPE
+    assert L.sq_absmax_reduce(None, sq.SQ_F16, 4, 16, 0, FAKE, None) == NULL
+    assert L.sq_absmax_reduce(FAKE, sq.SQ_F16, 4, 16, 0, None, None) == NULL
+    assert L.sq_absmax_reduce(FAKE + 8, sq.SQ_F16, 4, 16, 0, FAKE, None) == ALIGN
+    assert L.sq_absmax_reduce(None, sq.SQ_F16, 4, 0, 0, None, None) == OK       # no columns
+
+
+def test_scales_validation():
+    L = sq.lib()
+    for bad in (-0.1, 1.5, float("nan")):
+        assert L.sq_compute_scales(FAKE, FAKE, 8, bad, FAKE, FAKE, None, None) == ARG
+    assert L.sq_compute_scales(FAKE, FAKE, -1, 0.5, FAKE, FAKE, None, None) == SHAPE
+    assert L.sq_compute_scales(None, FAKE, 8, 0.5, FAKE, FAKE, None, None) == NULL
+    assert L.sq_compute_scales(FAKE, FAKE, 8, 0.5, FAKE + 2, FAKE, None, None) == ALIGN
+    assert L.sq_compute_scales(None, None, 0, 0.5, None, None, None, None) == OK
+
+
+def test_smooth_and_quantize_validation():
+    L = sq.lib()
+    assert L.sq_smooth_weights(FAKE, sq.SQ_F16, 8, 24, None, FAKE, FAKE, None) == SHAPE
+    assert L.sq_smooth_weights(FAKE, 5, 8, 32, None, FAKE, FAKE, None) == DTYPE
+    assert L.sq_smooth_weights(None, sq.SQ_F16, 8, 32, None, FAKE, FAKE, None) == NULL
+    assert L.sq_smooth_weights(FAKE, sq.SQ_F16, 8, 32, FAKE + 4, FAKE, FAKE, None) == ALIGN
+    assert L.sq_smooth_weights(None, sq.SQ_F16, 0, 32, None, None, None, None) == OK
+    assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 32, None, 3, None, FAKE, FAKE, None) == ARG
+    assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 32, None, sq.SQ_PER_TENSOR_STATIC, None,
+                             FAKE, FAKE, None) == NULL
+    assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 33, None, 1, None, FAKE, FAKE, None) == SHAPE
+    assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 32, None, 1, None, FAKE + 1, FAKE, None) == ALIGN
+    assert L.sq_quantize_act(None, sq.SQ_F16, 0, 32, None, 1, None, None, FAKE, None) == OK
+
+
+def test_gemm_validation():
+    L = sq.lib()
+    args = dict(xq=FAKE, wq=FAKE, M=4, N=4, K=32, xs=FAKE, per_row=1, ws=FAKE, y=FAKE,
+                y_dt=sq.SQ_F32, acc=None)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.sq_gemm_i8_dequant(a["xq"], a["wq"], a["M"], a["N"], a["K"], a["xs"],
+                                    a["per_row"], a["ws"], a["y"], a["y_dt"], a["acc"], None)
+
+    assert call(y_dt=9) == DTYPE
+    assert call(K=40) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(K=133152) == UNSUP
+    assert call(xq=None) == NULL
+    assert call(y=None) == NULL
+    assert call(wq=FAKE + 8) == ALIGN
+    assert call(y=FAKE + 2, y_dt=sq.SQ_F32) == ALIGN
+    assert call(M=0, xq=None, y=None) == OK
+    assert call(N=0) == OK
+
+
+def test_mixed_validation():
+    L = sq.lib()
+    need = L.sq_int8_mixed_matmul_workspace(2048, 4096)
+    assert need >= 2048 * 4096 + 2048 * 4 + 3 * 4096 * 4
+    assert need % 256 == 0
+
+    def call(thr=6.0, ws=FAKE, wsb=need, K=4096, x=FAKE):
+        return L.sq_int8_mixed_matmul(x, 2048, K, FAKE, FAKE, FAKE, 4096, thr, ws, wsb, FAKE,
+                                      sq.SQ_F16, None, None)
+
+    assert call(thr=0.0) == ARG
+    assert call(thr=-1.0) == ARG
+    assert call(thr=float("nan")) == ARG
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16) == ALIGN
+    assert call(K=4100) == SHAPE
+    assert call(x=None) == NULL
+
+
+def test_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        sq.absmax_reduce(torch.zeros(4, 16))

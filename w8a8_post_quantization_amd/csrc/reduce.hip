@@ -1,0 +1,211 @@
+// Column reductions and the smoothing-factor kernels.
+//
+// absmax_cols: per-channel abs-max of a row-major [rows, cols] matrix
+// ("x_j = max_i |X_ij|" and the weight-side w_j of the SmoothQuant tutorial
+// page, section 缩放因子; the calibration code of the lpnh.cn write-up §3.2).
+// Each lane owns one 16-byte column vector and keeps a running max over a
+// strided slab of rows; a block folds its four waves through LDS and merges
+// into the output with one atomicMax per column on the float bit pattern
+// (non-negative floats order like their unsigned bits).  Reads are
+// coalesced 1 KiB row segments per wave; the kernel is HBM-bound.
+//
+// compute_scales: s_j = max(max(x_j,1e-5)^a / max(w_j,1e-5)^(1-a), 1e-5),
+// powers and quotient in double rounded once; inv_s = fl(1/s); optional
+// static per-tensor step from max_j fl(x_j * inv_s_j).
+#include "sq_device.h"
+#include "sq_launch.h"
+
+namespace sq {
+
+__global__ void fill_zero_u32(uint32_t *p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          int64_t rows_per_block,
+                                                          uint32_t *__restrict__ out) {
+    constexpr int V = Vec<DT>::n;
+    __shared__ float red[4][kWave * V];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t cvec = cols / V;
+    const int64_t cv = (int64_t)blockIdx.x * kWave + lane;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
+
+    float m[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) m[i] = 0.0f;
+
+    if (cv < cvec) {
+        const uint4 *p = x + cv;
+        int64_t r = r0 + wave;
+        for (; r + 12 < r1; r += 16) {
+            uint4 v0 = p[r * cvec], v1 = p[(r + 4) * cvec];
+            uint4 v2 = p[(r + 8) * cvec], v3 = p[(r + 12) * cvec];
+            float f[V];
+            widen16<DT>(v0, f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+            widen16<DT>(v1, f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+            widen16<DT>(v2, f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+            widen16<DT>(v3, f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+        }
+        for (; r < r1; r += 4) {
+            float f[V];
+            widen16<DT>(p[r * cvec], f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) red[wave][i * kWave + lane] = m[i];
+    __syncthreads();
+    for (int c = threadIdx.x; c < kWave * V; c += 256) {
+        const float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        // red[.][i*64 + l] holds column (vector l, element i)
+        const int l = c & 63, i = c >> 6;
+        const int64_t col = ((int64_t)blockIdx.x * kWave + l) * V + i;
+        if (col < cols && v > 0.0f) atomicMax(&out[col], __float_as_uint(v));
+    }
+}
+
+void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
+                   float *amax, hipStream_t stream) {
+    if (cols == 0) return;
+    if (!accumulate)
+        fill_zero_u32<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream>>>(
+            reinterpret_cast<uint32_t *>(amax), cols);
+    if (rows == 0) return;
+    const int V = dt == F32 ? 4 : 8;
+    const int64_t cvec = cols / V;
+    const int64_t bx = (cvec + kWave - 1) / kWave;
+    // Aim for ~2048 blocks (8 per CU) with at least 64 rows per block.
+    int64_t by = (2048 + bx - 1) / bx;
+    const int64_t max_by = (rows + 63) / 64;
+    if (by > max_by) by = max_by;
+    if (by > 65535) by = 65535;
+    if (by < 1) by = 1;
+    const int64_t rpb = (rows + by - 1) / by;
+    by = (rows + rpb - 1) / rpb;
+    dim3 grid((unsigned)bx, (unsigned)by), block(256);
+    auto *out = reinterpret_cast<uint32_t *>(amax);
+    auto *xv = reinterpret_cast<const uint4 *>(x);
+    if (dt == F32)
+        absmax_cols_kernel<F32><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+    else if (dt == F16)
+        absmax_cols_kernel<F16><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+    else
+        absmax_cols_kernel<BF16><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+}
+
+__global__ __launch_bounds__(256) void scales_kernel(const float *__restrict__ act_amax,
+                                                     const float *__restrict__ w_amax,
+                                                     int64_t K, double alpha,
+                                                     float *__restrict__ s,
+                                                     float *__restrict__ inv_s) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    const float xc = act_amax[j] > 1e-5f ? act_amax[j] : 1e-5f;
+    const float wc = w_amax[j] > 1e-5f ? w_amax[j] : 1e-5f;
+    const double q = pow((double)xc, alpha) / pow((double)wc, 1.0 - alpha);
+    float sj = (float)q;
+    if (!(sj > 1e-5f)) sj = 1e-5f;
+    s[j] = sj;
+    inv_s[j] = 1.0f / sj;
+}
+
+// One block: a = max(max_j fl(x_j * inv_s_j), 1e-8); {a/127, 127/a}.
+__global__ __launch_bounds__(1024) void static_scale_kernel(const float *__restrict__ act_amax,
+                                                            const float *__restrict__ inv_s,
+                                                            int64_t K,
+                                                            float *__restrict__ out) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int64_t j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, act_amax[j] * inv_s[j]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+        for (int i = 1; i < 16; ++i) a = fmaxf(a, red[i]);
+        if (!(a > 1e-8f)) a = 1e-8f;
+        out[0] = a / 127.0f;
+        out[1] = 127.0f / a;
+    }
+}
+
+void launch_compute_scales(const float *act_amax, const float *w_amax, int64_t K, float alpha,
+                           float *s, float *inv_s, float *static_scale, hipStream_t stream) {
+    if (K > 0)
+        scales_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream>>>(
+            act_amax, w_amax, K, (double)alpha, s, inv_s);
+    if (static_scale)
+        static_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(act_amax, inv_s, K,
+                                                                 static_scale);
+}
+
+// LLM.int8() outlier list: O = ascending { j : colmax_j >= threshold }
+// (colmax is the column abs-max, so this is "some |x| reaches the
+// threshold"), mask_j = 0 for j in O else 1, plus |O|.  One block scans K in
+// chunks of 1024 with a ballot prefix count.
+__global__ __launch_bounds__(1024) void outlier_list_kernel(const float *__restrict__ colmax,
+                                                            int64_t K, float threshold,
+                                                            float *__restrict__ mask,
+                                                            int32_t *__restrict__ idx,
+                                                            int32_t *__restrict__ count) {
+    __shared__ int wave_cnt[16];
+    __shared__ int base_s;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) base_s = 0;
+    __syncthreads();
+    for (int64_t j0 = 0; j0 < K; j0 += 1024) {
+        const int64_t j = j0 + threadIdx.x;
+        const bool hit = j < K && colmax[j] >= threshold;
+        const uint64_t bal = __ballot(hit);
+        const int below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base_s;
+        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+        if (j < K) {
+            mask[j] = hit ? 0.0f : 1.0f;
+            if (hit) idx[off + below] = (int32_t)j;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += wave_cnt[w];
+            base_s += t;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *count = base_s;
+}
+
+__global__ void copy_i32_kernel(const int32_t *src, int32_t *dst) { *dst = *src; }
+__global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
+
+void launch_copy_i32(const int32_t *src, int32_t *dst, hipStream_t stream) {
+    copy_i32_kernel<<<dim3(1), dim3(1), 0, stream>>>(src, dst);
+}
+void launch_copy_f32(const float *src, float *dst, hipStream_t stream) {
+    copy_f32_kernel<<<dim3(1), dim3(1), 0, stream>>>(src, dst);
+}
+
+void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
+                         float *mask, int32_t *idx, int32_t *count, hipStream_t stream) {
+    launch_absmax(x, F16, M, K, 0, colmax, stream);
+    outlier_list_kernel<<<dim3(1), dim3(1024), 0, stream>>>(colmax, K, threshold, mask, idx,
+                                                            count);
+}
+
+}  // namespace sq

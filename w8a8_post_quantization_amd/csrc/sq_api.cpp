@@ -1,0 +1,174 @@
+// C ABI of the library (include/sq.h): argument validation on the host,
+// then kernel launches on the caller's stream.  No allocation, no
+// synchronization, no state besides the kernels themselves.
+#include "../../include/sq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "sq_launch.h"
+
+namespace {
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t esize(int dt) { return dt == SQ_F32 ? 4 : 2; }
+inline bool valid_dt(int dt) { return dt == SQ_F32 || dt == SQ_F16 || dt == SQ_BF16; }
+inline hipStream_t st(void *s) { return reinterpret_cast<hipStream_t>(s); }
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+int finish() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SQ_OK : SQ_ERR_HIP;
+}
+
+inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct MixedWs {
+    size_t xq, xs, colmax, mask, idx, count, total;
+};
+
+MixedWs mixed_layout(int64_t M, int64_t K) {
+    MixedWs w{};
+    size_t off = 0;
+    w.xq = off; off += round256((size_t)M * (size_t)K);
+    w.xs = off; off += round256((size_t)M * 4);
+    w.colmax = off; off += round256((size_t)K * 4);
+    w.mask = off; off += round256((size_t)K * 4);
+    w.idx = off; off += round256((size_t)K * 4);
+    w.count = off; off += 256;
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sq_status_str(int status) {
+    switch (status) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
+        case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: negative size or unsupported divisibility";
+        case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: element type not allowed";
+        case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: pointer not 16-byte aligned";
+        case SQ_ERR_ARG: return "SQ_ERR_ARG: invalid scalar argument";
+        case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+        case SQ_ERR_UNSUPPORTED: return "SQ_ERR_UNSUPPORTED: combination not implemented";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown sq_status";
+    }
+}
+
+int sq_version(void) { return 100; }
+
+int sq_absmax_reduce(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
+                     float *amax_out, void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return SQ_ERR_SHAPE;
+    if ((cols * (int64_t)esize(dt)) % 16 != 0) return SQ_ERR_SHAPE;
+    if (cols == 0) return SQ_OK;
+    if (!amax_out || (rows > 0 && !x)) return SQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(amax_out, 4)) return SQ_ERR_ALIGN;
+    sq::launch_absmax(x, dt, rows, cols, accumulate, amax_out, st(stream));
+    return finish();
+}
+
+int sq_compute_scales(const float *act_amax, const float *w_amax, int64_t K, float alpha,
+                      float *s, float *inv_s, float *static_scale, void *stream) {
+    if (K < 0 || K > kMaxDim) return SQ_ERR_SHAPE;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ARG;
+    if (K > 0 && (!act_amax || !w_amax || !s || !inv_s)) return SQ_ERR_NULL;
+    if (!aligned(act_amax, 4) || !aligned(w_amax, 4) || !aligned(s, 4) || !aligned(inv_s, 4) ||
+        !aligned(static_scale, 4))
+        return SQ_ERR_ALIGN;
+    if (K == 0 && !static_scale) return SQ_OK;
+    sq::launch_compute_scales(act_amax, w_amax, K, alpha, s, inv_s, static_scale, st(stream));
+    return finish();
+}
+
+int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K, const float *s, int8_t *wq,
+                      float *w_scale, void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (N == 0) return SQ_OK;
+    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(w_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_quant_rows(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream));
+    return finish();
+}
+
+int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *inv_s, int mode,
+                    const float *static_scale, int8_t *xq, float *x_scale, void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
+    if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;
+    if (M > 0 && K > 0 && (!x || !xq)) return SQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(inv_s, 16) || !aligned(x_scale, 4) ||
+        !aligned(static_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_quant_rows(x, dt, M, K, inv_s, mode == SQ_PER_TOKEN_DYNAMIC, static_scale, xq,
+                          x_scale, st(stream));
+    return finish();
+}
+
+int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                       const float *x_scale, int x_scale_per_row, const float *w_scale, void *y,
+                       int y_dt, int32_t *acc_out, void *stream) {
+    if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
+        return SQ_ERR_SHAPE;
+    if (K > 133143) return SQ_ERR_UNSUPPORTED;  // 127*127*K must fit int32
+    if (M == 0 || N == 0) return SQ_OK;
+    if (!x_scale || !w_scale || !y || (K > 0 && (!xq || !wq))) return SQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+        !aligned(y, esize(y_dt)) || !aligned(acc_out, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_gemm(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
+                    acc_out, nullptr, st(stream));
+    return finish();
+}
+
+size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K) {
+    if (M < 0 || K < 0) return 0;
+    return mixed_layout(M, K).total;
+}
+
+int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                         const float *w_scale, const void *w_f16, int64_t N, float threshold,
+                         void *workspace, size_t workspace_bytes, void *y, int y_dt,
+                         int32_t *n_outliers_out, void *stream) {
+    if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
+        return SQ_ERR_SHAPE;
+    if (K > 133143) return SQ_ERR_UNSUPPORTED;
+    if (!(threshold > 0.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (M == 0 || N == 0) return SQ_OK;
+    if (!x || !wq || !w_scale || !w_f16 || !y) return SQ_ERR_NULL;
+    const MixedWs L = mixed_layout(M, K);
+    if (!workspace || workspace_bytes < L.total) return SQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(w_f16, 16) || !aligned(w_scale, 4) ||
+        !aligned(y, esize(y_dt)) || !aligned(n_outliers_out, 4))
+        return SQ_ERR_ALIGN;
+    char *ws = static_cast<char *>(workspace);
+    auto *xq = reinterpret_cast<int8_t *>(ws + L.xq);
+    auto *xs = reinterpret_cast<float *>(ws + L.xs);
+    auto *colmax = reinterpret_cast<float *>(ws + L.colmax);
+    auto *mask = reinterpret_cast<float *>(ws + L.mask);
+    auto *idx = reinterpret_cast<int32_t *>(ws + L.idx);
+    auto *count = reinterpret_cast<int32_t *>(ws + L.count);
+    hipStream_t s = st(stream);
+    sq::launch_outlier_prep(x, M, K, threshold, colmax, mask, idx, count, s);
+    sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
+    sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
+                      count};
+    sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, nullptr, &side, s);
+    if (n_outliers_out) sq::launch_copy_i32(count, n_outliers_out, s);
+    return finish();
+}
+
+}  // extern "C"

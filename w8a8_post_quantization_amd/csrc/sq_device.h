@@ -1,0 +1,84 @@
+// Device-side helpers shared by the gfx950 kernels: 16-byte vector loads,
+// element widening, wave-level reductions and the int8 quantizer step.
+// Compiled with -ffp-contract=off: every a*b and a+b below is its own
+// IEEE binary32 operation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+constexpr int kWave = 64;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
+
+enum Dt { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Element count of one 16-byte vector of each type.
+template <int DT> struct Vec { static constexpr int n = DT == F32 ? 4 : 8; };
+
+// Widen the elements of one 16-byte vector to fp32 (exact for all types).
+template <int DT>
+__device__ __forceinline__ void widen16(const uint4 &v, float *out) {
+    if constexpr (DT == F32) {
+        out[0] = __uint_as_float(v.x);
+        out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z);
+        out[3] = __uint_as_float(v.w);
+    } else if constexpr (DT == F16) {
+        half8 h = __builtin_bit_cast(half8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = (float)h[i];
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Round half to even (v_rndne_f32), clamp to [-127, 127], as int.
+__device__ __forceinline__ int quant_i8(float v, float inv) {
+    float r = __builtin_rintf(v * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// Narrow fp32 to the output type with round-to-nearest-even.
+template <int DT> struct OutT;
+template <> struct OutT<F32> { using T = float; };
+template <> struct OutT<F16> { using T = _Float16; };
+template <> struct OutT<BF16> { using T = __bf16; };
+
+// The empty asm pins the fp32 value in a register: without it the compiler
+// may fold "fp32 multiply, then convert to fp16" into one mixed-precision
+// fma that rounds the exact product once, which differs from rounding to
+// fp32 first whenever the fp32 result is an fp16 tie.
+__device__ __forceinline__ float materialize(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int DT>
+__device__ __forceinline__ typename OutT<DT>::T narrow(float v) {
+    if constexpr (DT == F32) return v;
+    else return (typename OutT<DT>::T)materialize(v);
+}
+
+}  // namespace sq

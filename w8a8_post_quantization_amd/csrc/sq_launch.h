@@ -1,0 +1,45 @@
+// Internal launchers behind the C ABI (include/sq.h).  Arguments arrive
+// validated; each launcher only enqueues kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sq {
+
+void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
+                   float *amax, hipStream_t stream);
+
+void launch_compute_scales(const float *act_amax, const float *w_amax, int64_t K, float alpha,
+                           float *s, float *inv_s, float *static_scale, hipStream_t stream);
+
+// Per-row quantization of fp(x) * mul (mul may be NULL): a3 uses it with
+// per_row = true for weights, a4 for activations (either mode), a6 for the
+// outlier-masked rows.
+void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
+                       int dynamic, const float *static_scale, int8_t *q, float *scale,
+                       hipStream_t stream);
+
+struct SideTerm {  // LLM.int8() fp16 side product over outlier columns
+    const uint16_t *x16;   // [M, K]
+    const uint16_t *w16;   // [N, K]
+    const int32_t *idx;    // device list of outlier columns, ascending
+    const int32_t *count;  // device |O|
+};
+
+void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                 const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
+                 int32_t *acc_out, const SideTerm *side, hipStream_t stream);
+
+// LLM.int8() preparation: column abs-max of x into colmax, then the mask
+// (1.0 keep / 0.0 outlier), the ascending O list and its count.
+void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
+                         float *mask, int32_t *idx, int32_t *count, hipStream_t stream);
+
+// Tiny device-to-device copies done by a kernel (no copy-engine or memset
+// nodes, so the calls stay capturable in a HIP graph).
+void launch_copy_i32(const int32_t *src, int32_t *dst, hipStream_t stream);
+void launch_copy_f32(const float *src, float *dst, hipStream_t stream);
+
+}  // namespace sq
