@@ -135,7 +135,9 @@ GEMM_CASES = [
     (257, 300, 1024, "bf16", 1, None), (256, 1000, 7168, "bf16", 1, None),
     (129, 511, 2064, "f32", 0, None), (600, 700, 384, "f16", 1, "0"),
     (300, 520, 512, "f32", 1, "1"), (260, 390, 256, "bf16", 0, "2"),
-    (513, 257, 1040, "f16", 1, "0"),
+    (513, 257, 1040, "f16", 1, "0"), (70, 300, 128, "bf16", 1, "1"), (96, 96, 64, "f32", 1, "0"),
+    (2048, 512, 4096, "f16", 1, None), (300, 300, 128, "f16", 1, "0"), (129, 260, 256, "f32", 1, "2"),
+    (264, 136, 384, "bf16", 1, "1"),
     # skinny (decode) path
     (1, 1000, 8192, "f16", 1, None), (8, 333, 512, "f32", 1, None),
     (16, 64, 1024, "f32", 0, None), (17, 100, 256, "bf16", 1, None),

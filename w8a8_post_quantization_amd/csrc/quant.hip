@@ -22,7 +22,6 @@
 
 namespace sq {
 
-constexpr int kMaxIt = 16;
 
 template <int DT>
 __device__ __forceinline__ void load_mul(const float *__restrict__ mul, int64_t e0, float *m) {
@@ -38,14 +37,27 @@ __device__ __forceinline__ void load_mul(const float *__restrict__ mul, int64_t 
     }
 }
 
-template <int DT, bool HAS_MUL>
+extern __shared__ float4 smul4[];
+
+template <int DT, bool HAS_MUL, bool MUL_LDS>
 __device__ __forceinline__ void scaled(const uint4 &raw, const float *__restrict__ mul,
                                        int64_t e0, float *v) {
     constexpr int V = Vec<DT>::n;
     widen16<DT>(raw, v);
     if constexpr (HAS_MUL) {
         float m[V];
-        load_mul<DT>(mul, e0, m);
+        if constexpr (MUL_LDS) {
+#pragma unroll
+            for (int i = 0; i < V / 4; ++i) {
+                const float4 t = smul4[e0 / 4 + i];
+                m[4 * i] = t.x;
+                m[4 * i + 1] = t.y;
+                m[4 * i + 2] = t.z;
+                m[4 * i + 3] = t.w;
+            }
+        } else {
+            load_mul<DT>(mul, e0, m);
+        }
 #pragma unroll
         for (int i = 0; i < V; ++i) v[i] = v[i] * m[i];
     }
@@ -68,76 +80,98 @@ __device__ __forceinline__ void store_q(int8_t *__restrict__ q, int64_t e0, cons
     }
 }
 
-template <int DT, bool HAS_MUL, bool DYN, bool IN_REGS>
+// mul comes from LDS when it fits (K <= kMulLds floats): it is read once per
+// block instead of once per row, and - more important - reading it from
+// global memory inside the store loop would make each iteration wait for
+// the earlier stores as well (vmcnt counts loads and stores alike).
+constexpr int kMulLds = 16384;
+
+// ITS > 0: the row is held in registers, ITS 16-byte vectors per lane, with
+// out-of-range indices clamped to the row's last vector (loaded but not
+// used) so every load is unconditional: a load inside a lane-divergent
+// branch makes the compiler wait for all earlier memory operations first,
+// which would serialize the row's loads.  ITS = 0: rows longer than
+// 16 x 64 vectors, streamed twice (the second pass hits L2).
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
-                                                         const float *__restrict__ mul,
+                                                         const float *__restrict__ mul_g,
                                                          const float *__restrict__ static_scale,
                                                          int8_t *__restrict__ q,
-                                                         float *__restrict__ scale) {
+                                                         float *__restrict__ scale,
+                                                         int rows_per_wave) {
     constexpr int V = Vec<DT>::n;
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (!DYN && blockIdx.x == 0 && threadIdx.x == 0) scale[0] = static_scale[0];
-    if (r >= rows) return;
+    // The multiplier's address space is fixed at compile time (an LDS or a
+    // global pointer), so its reads are ds_read / global_load, never flat.
+    const float *mul = mul_g;
+    if constexpr (HAS_MUL && MUL_LDS) {
+        const float4 *src = reinterpret_cast<const float4 *>(mul_g);
+        for (int64_t i = threadIdx.x; i < K / 4; i += 256) smul4[i] = src[i];
+        __syncthreads();
+    }
     const int64_t nvec = K / V;
-    const uint4 *xr = x + r * nvec;
-    int8_t *qr = q + r * K;
+    const float inv_static = DYN ? 0.0f : static_scale[1];
 
-    if constexpr (DYN) {
-        uint4 buf[IN_REGS ? kMaxIt : 1];
-        float a = 0.0f;
-        if constexpr (IN_REGS) {
+    for (int rw = 0; rw < rows_per_wave; ++rw) {
+        const int64_t r = ((int64_t)blockIdx.x * rows_per_wave + rw) * 4 + wave;
+        if (r >= rows) break;
+        const uint4 *xr = x + r * nvec;
+        int8_t *qr = q + r * K;
+        if constexpr (DYN && ITS > 0) {
+            uint4 buf[ITS];
 #pragma unroll
-            for (int it = 0; it < kMaxIt; ++it) {
+            for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
-                if (vi < nvec) buf[it] = xr[vi];
+                buf[it] = xr[vi < nvec ? vi : nvec - 1];
             }
+            float a = 0.0f;
 #pragma unroll
-            for (int it = 0; it < kMaxIt; ++it) {
+            for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
-                if (vi < nvec) {
-                    float v[V];
-                    scaled<DT, HAS_MUL>(buf[it], mul, vi * V, v);
-#pragma unroll
-                    for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
-                }
-            }
-        } else {
-            for (int64_t vi = lane; vi < nvec; vi += kWave) {
+                const int64_t vc = vi < nvec ? vi : nvec - 1;
                 float v[V];
-                scaled<DT, HAS_MUL>(xr[vi], mul, vi * V, v);
+                scaled<DT, HAS_MUL, MUL_LDS>(buf[it], mul, vc * V, v);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
-        }
-        a = wave_max(a);
-        if (!(a > 1e-8f)) a = 1e-8f;
-        const float inv = 127.0f / a;
-        if (lane == 0) scale[r] = a / 127.0f;
-        if constexpr (IN_REGS) {
+            a = wave_max(a);
+            if (!(a > 1e-8f)) a = 1e-8f;
+            const float inv = 127.0f / a;
+            if (lane == 0) scale[r] = a / 127.0f;
 #pragma unroll
-            for (int it = 0; it < kMaxIt; ++it) {
+            for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
                 if (vi < nvec) {
                     float v[V];
-                    scaled<DT, HAS_MUL>(buf[it], mul, vi * V, v);
+                    scaled<DT, HAS_MUL, MUL_LDS>(buf[it], mul, vi * V, v);
                     store_q<DT>(qr, vi * V, v, inv);
                 }
+            }
+        } else if constexpr (DYN) {
+            float a = 0.0f;
+            for (int64_t vi = lane; vi < nvec; vi += kWave) {
+                float v[V];
+                scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
+#pragma unroll
+                for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
+            }
+            a = wave_max(a);
+            if (!(a > 1e-8f)) a = 1e-8f;
+            const float inv = 127.0f / a;
+            if (lane == 0) scale[r] = a / 127.0f;
+            for (int64_t vi = lane; vi < nvec; vi += kWave) {
+                float v[V];
+                scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
+                store_q<DT>(qr, vi * V, v, inv);
             }
         } else {
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
-                scaled<DT, HAS_MUL>(xr[vi], mul, vi * V, v);
-                store_q<DT>(qr, vi * V, v, inv);
+                scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
+                store_q<DT>(qr, vi * V, v, inv_static);
             }
-        }
-    } else {
-        const float inv = static_scale[1];
-        for (int64_t vi = lane; vi < nvec; vi += kWave) {
-            float v[V];
-            scaled<DT, HAS_MUL>(xr[vi], mul, vi * V, v);
-            store_q<DT>(qr, vi * V, v, inv);
         }
     }
 }
@@ -145,15 +179,32 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
 template <int DT, bool HAS_MUL, bool DYN>
 static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream) {
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    // Rows per wave: enough blocks to fill the chip (>= ~1024), more rows
+    // per block when there are plenty, so the multiplier is staged rarely.
+    int64_t rpw = rows / (4 * 1024);
+    if (rpw < 1) rpw = 1;
+    if (rpw > 8) rpw = 8;
+    const int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
+    const bool mul_lds = HAS_MUL && K <= kMulLds;
+    const size_t shmem = mul_lds ? (size_t)K * sizeof(float) : 0;
+    dim3 grid((unsigned)blocks), block(256);
     auto *xv = reinterpret_cast<const uint4 *>(x);
-    const bool in_regs = K / Vec<DT>::n <= (int64_t)kMaxIt * kWave;
-    if (DYN && in_regs)
-        quant_rows_kernel<DT, HAS_MUL, DYN, true>
-            <<<grid, block, 0, stream>>>(xv, rows, K, mul, static_scale, q, scale);
-    else
-        quant_rows_kernel<DT, HAS_MUL, DYN, false>
-            <<<grid, block, 0, stream>>>(xv, rows, K, mul, static_scale, q, scale);
+    const int64_t nit = (K / Vec<DT>::n + kWave - 1) / kWave;  // vectors per lane
+    const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
+#define SQ_Q(ITS, LDS)                                                                     \
+    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS><<<grid, block, shmem, stream>>>(         \
+        xv, rows, K, mul, static_scale, q, scale, (int)rpw)
+#define SQ_QL(ITS) \
+    do { if (mul_lds) SQ_Q(ITS, true); else SQ_Q(ITS, false); } while (0)
+    switch (its) {
+        case 2: SQ_QL(2); break;
+        case 4: SQ_QL(4); break;
+        case 8: SQ_QL(8); break;
+        case 16: SQ_QL(16); break;
+        default: SQ_QL(0); break;
+    }
+#undef SQ_QL
+#undef SQ_Q
 }
 
 template <int DT>
