@@ -127,13 +127,13 @@ def test_decoder_1024(torch, alpha):
 
 def test_decode_8192(torch):
     """Calibrate on X_cal [512,8192], quantize W [28672,8192], then decode
-    GEMMs at M = 1, 8, 32 with per-token X and fp16 out (skinny kernel)."""
+    GEMMs at M = 1, 8, 16, 32 with per-token X and fp16 out (decode kernel)."""
     cfg = synth.decode_8192(32)
     W = cfg["W"]
     log("decode_8192 stats")
     s_o, inv_o = _stats(torch, cfg["X_cal"], W, 0.5)
     wq, ws, wq_o, ws_o = _weights(torch, W, s_o)
-    for M in (1, 8, 32):
+    for M in (1, 8, 16, 32):
         X = cfg["X"][:M]
         log(f"decode_8192 M={M}")
         xq, xs, xq_o, xs_o = _act(torch, X, inv_o)

@@ -5,19 +5,21 @@
 // xdnf.cn LLM.int8() explainer §2.1: int32 accumulation and the c_x (x) c_w
 // outer product; §2.2 for the fp16 side product over outlier columns).
 //
-// Two kernels, same bits:
-//  * gemm_tile: M > 32.  256 threads = 4 waves, block tile BM x BN, K staged
-//    through LDS 128 bytes at a time, double-buffered (global -> registers
-//    -> LDS while the MFMAs consume the other buffer).  Each wave owns a
-//    (BM/WM) x (BN/WN) sub-tile of v_mfma_i32_32x32x32_i8 fragments.  Both
-//    operands are K-contiguous, so a lane's 16-byte MFMA operand is one
-//    ds_read_b128.  LDS rows are 128 bytes; chunk c of row r lives at slot
-//    c ^ swz(r), which keeps ds_write_b128 and ds_read_b128 free of bank
-//    conflicts whether 8 or 16 lanes are served per cycle.
-//  * gemm_skinny: M <= 32 (decode).  HBM-bound on the weight stream: a block
-//    owns 32 weight rows, its 4 waves split K, v_mfma_i32_16x16x64_i8 with
-//    weight rows as the MFMA rows and tokens (padded to 16 / 32) as columns;
-//    int32 partials are summed exactly through LDS.
+// Three kernels, same bits:
+//  * gemm_pp: M > 32 and K % 128 == 0 (every prefill shape).  Block tile
+//    BM x BN of 4 or 8 waves, each wave a (BM/WM) x (BN/WN) sub-tile of
+//    v_mfma_i32_32x32x32_i8 fragments.  K is streamed 128 bytes a stage into
+//    a ring of LDS stages with direct-to-LDS loads (no register staging),
+//    and the MFMAs of one stage interleave with the LDS reads of the next.
+//  * gemm_tile: M > 32 with K % 128 != 0.  Same tiles, K staged through
+//    registers into a double-buffered LDS tile, tail loads clamped.
+//    In both, LDS rows are 128 bytes and chunk c of row r lives at slot
+//    c ^ swz(r), which keeps the 16-byte LDS reads free of bank conflicts.
+//  * gemm_dec: M <= 32 (decode), bound by the weight stream: a block owns
+//    16..64 weight rows, its 4 waves split K and stream it through private
+//    LDS rings with coalesced direct-to-LDS loads; v_mfma_i32_16x16x64_i8
+//    with weight rows as the MFMA rows and tokens (padded to 16 / 32) as
+//    columns; int32 partials are summed exactly through LDS.
 //
 // An integer dot product does not depend on the order of its terms, so the
 // assignment of K bytes to MFMA lanes only has to be the same for both
@@ -318,6 +320,18 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_base) {
         : "memory", "m0");
 }
 
+// The same with the nontemporal hint, for data read once (a weight stream
+// that should not displace reused lines in the caches).
+__device__ __forceinline__ void lds_dma16_nt(const void *g, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt"
+        :
+        : "v"(g), "s"(lds_base)
+        : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) leaving lgkmcnt / expcnt alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -362,6 +376,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                                             int m0, int n0) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NT = 64 * WM * WN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int fr = lane & 31, fh = lane >> 5;
@@ -382,12 +397,12 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            for (int e = tid; e < BM * 32; e += 256) {
+            for (int e = tid; e < BM * 32; e += NT) {
                 const int r = e >> 5, t = e & 31;
                 const int gr = m0 + r < M ? m0 + r : M - 1;
                 xo[r * 33 + t] = t < tn ? h2f(p.x16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
             }
-            for (int e = tid; e < BN * 32; e += 256) {
+            for (int e = tid; e < BN * 32; e += NT) {
                 const int r = e >> 5, t = e & 31;
                 const int gr = n0 + r < N ? n0 + r : N - 1;
                 wo[r * 33 + t] = t < tn ? h2f(p.w16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
@@ -471,34 +486,42 @@ __device__ __forceinline__ void sched_tail() {
     }
 }
 
-// K % 128 == 0.  K is staged 128 bytes at a time through an ST-deep LDS ring
-// filled by direct-to-LDS loads (global_load_lds_dwordx4): each wave
-// instruction moves 8 rows x 128 bytes, so every request to L2 is a whole
-// 128-byte line (with 64-byte stages each line was fetched as two 64-byte
-// requests, and the number of requests the vector L1 keeps in flight - not
-// bytes or L2 bandwidth - capped the per-CU feed rate).  Lane l writes LDS
-// bytes [16 l, 16 l + 16) of its 1 KiB block; the swizzle (see swz) is
-// applied by choosing which global chunk each lane fetches.  All ST stages are
-// in flight.
+// K % 128 == 0.  K is staged 128 bytes at a time through two LDS rings
+// filled by direct-to-LDS loads (global_load_lds_dwordx4): an activation
+// ring of STA slots and a weight ring of STB slots.  Each wave instruction
+// moves 8 rows x 128 bytes, so every request to L2 is a whole 128-byte line
+// (64-byte stages fetched each line as two requests, and the number of
+// requests the vector L1 keeps in flight capped the feed rate).  Lane l
+// writes LDS bytes [16 l, 16 l + 16) of its 1 KiB block; the swizzle (see
+// swz) is applied by choosing which global chunk each lane fetches.
+//
+// The rings differ in depth because the operands differ in latency: the
+// activation tile is re-read by every block from L2, while each weight byte
+// comes once from HBM, so weights are prefetched STB - 1 stages ahead
+// (about 2 us at full MFMA rate when STB = 5) and activations one stage.
+// Loads complete in issue order; per iteration the kernel issues the
+// activation stage kt + STA, then the weight stage kt + STB, which fixes
+// the vmcnt values below.  With STB == STA the rings move in lockstep.
 //
 // Each stage is consumed as four 32-byte quarters with ping-pong fragment
 // registers: a quarter's LDS reads overlap the previous quarter's MFMAs, and
 // after the stage barrier the next stage's first reads overlap the last
-// quarter's MFMAs, so the MFMA pipe does not wait for a full LDS round trip.
-// Weight rows are the MFMA A operand (see epilogue_nt).
-template <int BM, int BN, int WM, int WN, int ST, int YDT, bool SIDE>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_pp(
-    GemmArgs p) {
+// quarter's MFMAs.  Weight rows are the MFMA A operand (see epilogue_nt).
+template <int BM, int BN, int WM, int WN, int STA, int STB, int YDT, bool SIDE>
+__global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(1, 4))) void
+gemm_pp(GemmArgs p) {
     constexpr int BK = 128;
+    constexpr int NW = WM * WN;  // waves
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int LA = BM / 32, LB = BN / 32;  // load instructions per wave per stage
+    constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);  // load instructions per wave per stage
     constexpr int L = LA + LB;
-    constexpr int STAGE = (BM + BN) * BK;
-    static_assert(WM * WN == 4 && FM >= 1 && FN >= 1, "tile");
-    static_assert(ST >= 2 && (ST - 1) * L < 64, "pipeline depth");
+    constexpr int SA = BM * BK, SB = BN * BK;  // bytes of one stage of each operand
+    static_assert((NW == 4 || NW == 8) && FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile");
+    static_assert(STA >= 2 && (STB == STA || (STA == 2 && STB > STA)), "ring depths");
+    static_assert((STB - 1) * LB + STA * LA < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) int8_t smem[ST * STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STA * SA + STB * SB];
     __shared__ __attribute__((aligned(16))) float sx[BM], sw[BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -525,20 +548,25 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) 
         const int gr = n0 + row < N ? n0 + row : N - 1;
         b_src[j] = p.wq + (int64_t)gr * K + c * 16;
     }
-    // Stage s of K into ring slot `slot`: this wave's A blocks are the 1 KiB
-    // blocks wave*LA + j of the slot, its B blocks follow the A tile at
-    // wave*LB + j (the same blocks the global rows above were chosen for).
+    // This wave's blocks: activation blocks wave*LA + j of an A slot, weight
+    // blocks wave*LB + j of a B slot (the blocks the rows above were chosen
+    // for).  LDS byte addresses, wave-uniform for M0.
     const uint32_t waveu = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds_a = (uint32_t)(uintptr_t)(lds_void_t *)smem + waveu * (LA * 1024u);
-    const uint32_t lds_b =
-        (uint32_t)(uintptr_t)(lds_void_t *)smem + (uint32_t)(BM * BK) + waveu * (LB * 1024u);
-    auto issue = [&](int s, int slot) {
-        const uint32_t so = (uint32_t)(slot * STAGE);
-        const int k0 = s * BK;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    const uint32_t lds_a = lds0 + waveu * (LA * 1024u);
+    const uint32_t lds_b = lds0 + (uint32_t)(STA * SA) + waveu * (LB * 1024u);
+    const int nk = K / BK;
+    auto issue_a = [&](int s) {  // activation stage s (past the end: the last one)
+        const int sc = s < nk ? s : nk - 1;
+        const uint32_t base = lds_a + (uint32_t)((s % STA) * SA);
 #pragma unroll
-        for (int j = 0; j < LA; ++j) lds_dma16(a_src[j] + k0, lds_a + so + (uint32_t)(j * 1024));
+        for (int j = 0; j < LA; ++j) lds_dma16(a_src[j] + sc * BK, base + (uint32_t)(j * 1024));
+    };
+    auto issue_b = [&](int s) {
+        const int sc = s < nk ? s : nk - 1;
+        const uint32_t base = lds_b + (uint32_t)((s % STB) * SB);
 #pragma unroll
-        for (int j = 0; j < LB; ++j) lds_dma16(b_src[j] + k0, lds_b + so + (uint32_t)(j * 1024));
+        for (int j = 0; j < LB; ++j) lds_dma16(b_src[j] + sc * BK, base + (uint32_t)(j * 1024));
     };
 
     const int fr = lane & 31, fh = lane >> 5;
@@ -547,13 +575,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) 
 #pragma unroll
     for (int q = 0; q < 4; ++q) off[q] = ((2 * q + fh) ^ fsw) << 4;
     auto read_frags = [&](int s, int q, int4v (&xf)[FM], int4v (&wf)[FN]) {
-        const int8_t *base = smem + (s % ST) * STAGE + off[q];
+        const int8_t *ab = smem + (s % STA) * SA + off[q];
+        const int8_t *bb = smem + STA * SA + (s % STB) * SB + off[q];
 #pragma unroll
         for (int f = 0; f < FM; ++f)
-            xf[f] = *reinterpret_cast<const int4v *>(base + (wm * WTM + f * 32 + fr) * BK);
+            xf[f] = *reinterpret_cast<const int4v *>(ab + (wm * WTM + f * 32 + fr) * BK);
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-            wf[f] = *reinterpret_cast<const int4v *>(base + BM * BK + (wn * WTN + f * 32 + fr) * BK);
+            wf[f] = *reinterpret_cast<const int4v *>(bb + (wn * WTN + f * 32 + fr) * BK);
     };
 
     int16v acc[FN][FM];
@@ -575,18 +604,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) 
     // interleave: a wave issues in order, so a ds_read (or direct load)
     // queued behind an MFMA that waits for the matrix core cannot issue; the
     // sched_group_barrier sequences place one memory instruction after each
-    // MFMA, letting LDS traffic and the next stage's loads run under the
-    // MFMAs.  Past the last stage, the free ring slot is refilled with the
-    // last stage (never read), which keeps every iteration's load count -
-    // and so the vmcnt arithmetic - the same; all loads are drained before
-    // the epilogue.
-    constexpr int RQ = FM + FN;       // ds_read_b128 per quarter
-    constexpr int MQ = FM * FN;       // MFMAs per quarter
+    // MFMA.  Past the last stage, free ring slots are refilled with the last
+    // stage (never read), which keeps every iteration's load count - and so
+    // the vmcnt arithmetic - the same; all loads are drained before the
+    // epilogue.
+    constexpr int RQ = FM + FN;  // ds_read_b128 per quarter
+    constexpr int MQ = FM * FN;  // MFMAs per quarter
     static_assert(RQ <= MQ, "one read per MFMA slot");
-    const int nk = K / BK;
+    if constexpr (STB > STA) {
+        // prologue: all weight stages first, then the activation stages
 #pragma unroll
-    for (int s = 0; s < ST; ++s) issue(s < nk ? s : nk - 1, s);
-    wait_vmcnt<(ST - 1) * L>();
+        for (int s = 0; s < STB; ++s) issue_b(s);
+#pragma unroll
+        for (int s = 0; s < STA; ++s) issue_a(s);
+        wait_vmcnt<(STA - 1) * LA>();  // A0 (and every B before it) landed
+    } else {
+#pragma unroll
+        for (int s = 0; s < STA; ++s) {
+            issue_a(s);
+            issue_b(s);
+        }
+        wait_vmcnt<(STA - 1) * L>();
+    }
     lds_barrier();
     int4v xa[FM], wa[FN], xb[FM], wb[FN];
     read_frags(0, 0, xa, wa);
@@ -606,10 +645,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) 
             }
             __builtin_amdgcn_sched_group_barrier(0x008, MQ - RQ, 0);
         }
-        wait_vmcnt<(ST - 2) * L>();  // stage kt + 1 has landed
-        lds_barrier();               // every wave has read stage kt: its slot is free
+        // Stage kt + 1 of both operands must have landed.
+        if constexpr (STB > STA) {
+            // A(kt+1) was the last activation load; after it only B(kt-1+STB)
+            if (kt == 0) wait_vmcnt<0>();
+            else wait_vmcnt<LB>();
+        } else {
+            wait_vmcnt<(STA - 2) * L>();
+        }
+        lds_barrier();  // every wave has read stage kt: its slots are free
         read_frags(kt + 1, 0, xa, wa);
-        issue(kt + ST < nk ? kt + ST : nk - 1, kt % ST);
+        issue_a(kt + STA);
+        issue_b(kt + STB);
         mma(xb, wb);
         sched_tail<MQ, RQ, L, 0>();  // MFMA, DS read, direct loads, ...
     }
@@ -619,127 +666,197 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) 
     epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0);
 }
 
-// ---------------------------------------------------------------- skinny
+// ---------------------------------------------------------------- decode
 
-template <int FT, int YDT>
-__global__ __launch_bounds__(256) void gemm_skinny(GemmArgs p) {
-    constexpr int NR = 32;  // weight rows per block: two 16-row fragments
-    __shared__ int red[4][2][FT][64 * 4];
+// Decode GEMM (M <= 32), bound by the weight stream.  A block owns 16*NF
+// weight rows; its 4 waves split K and each streams its K range through a
+// private ring of S LDS stages with direct-to-LDS loads.  A stage holds
+// U 64-byte K steps of the 16*NF weight rows and the 16*FT token rows.
+//
+// Why LDS: in MFMA operand layout the 16 lanes of a quarter-wave hold 16
+// different rows, so a 16-byte-per-lane register load touches 16 cache
+// lines per quarter-wave (64 tag lookups per 1 KB instruction) and the
+// texture data path, not HBM, sets the rate.  Here each 1 KB load has a
+// quarter-wave read one contiguous row span (16 / U rows of 64*U bytes per
+// load), and the fragments are read back from LDS in operand layout.  Chunk
+// c of row r sits at position c ^ f(r) of its row so that the 16 rows a
+// quarter-wave reads fall in distinct banks.
+//
+// K order inside the MFMA is free for integer sums: both operands use
+// "lane group g of step s holds bytes 64 s + 16 g .. + 15 of the stage".
+template <int U>
+__device__ __forceinline__ int dec_swz(int r) {
+    return (r / (4 / U)) & (4 * U - 1);
+}
+
+// Wait until at most `later` stages of P loads each are in flight
+// (later <= L; vmcnt takes an immediate, hence the unrolled choice).
+template <int L, int P>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (L == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= L) wait_vmcnt<L * P>();
+        else wait_stages<L - 1, P>(later);
+    }
+}
+
+template <int NF, int FT, int U, int S, int YDT, bool NT>
+__global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
+    static_assert(U == 1 || U == 2 || U == 4, "stage width");
+    static_assert(S >= 2 && S <= 6, "ring depth");
+    constexpr int NR = 16 * NF;
+    constexpr int NFR = NF + FT;                 // fragments per stage
+    constexpr int P = NFR * U;                   // 1 KB loads per stage
+    constexpr int SLOT = P * 1024;               // one stage of one wave
+    constexpr int RING = S * SLOT;
+    constexpr int RED = 4 * NF * FT * 1024;      // int32 partial sums of 4 waves
+    constexpr int LDSB = 4 * RING > RED ? 4 * RING : RED;
+    constexpr int RPI = 16 / U;                  // rows per 1 KB load
+    constexpr int CPR = 4 * U;                   // 16-byte chunks per row per stage
+    __shared__ __align__(16) char smem[LDSB];
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = p.M, N = p.N, K = p.K;
     const int n0 = blockIdx.x * NR;
-    const int r16 = lane & 15, kg = (lane >> 4) * 16;
 
-    const int8_t *wrow[2];
+    // Loader side: in load u of fragment j, lane l fetches row u*RPI + l/CPR
+    // of the fragment, chunk (l % CPR) ^ f(row) of the stage.
+    const int lr = lane / CPR, lp = lane % CPR;
+    const int8_t *src[NFR][U];
+    int coff[U];  // byte offset of the lane's chunk inside a stage
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const int n = n0 + f * 16 + r16;
-        wrow[f] = p.wq + (int64_t)(n < N ? n : N - 1) * K + kg;
+    for (int u = 0; u < U; ++u) {
+        const int r = u * RPI + lr;
+        const int c = lp ^ dec_swz<U>(r);
+        coff[u] = 16 * c;
+#pragma unroll
+        for (int j = 0; j < NFR; ++j) {
+            const int8_t *row;
+            if (j < NF) {
+                const int n = n0 + j * 16 + r;
+                row = p.wq + (int64_t)(n < N ? n : N - 1) * K;
+            } else {
+                const int m = (j - NF) * 16 + r;
+                row = p.xq + (int64_t)(m < M ? m : M - 1) * K;
+            }
+            src[j][u] = row;
+        }
     }
-    const int8_t *xrow[FT];
-#pragma unroll
-    for (int t = 0; t < FT; ++t) {
-        const int m = t * 16 + r16;
-        xrow[t] = p.xq + (int64_t)(m < M ? m : M - 1) * K + kg;
-    }
 
-    int4v acc[2][FT];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int t = 0; t < FT; ++t) acc[f][t] = int4v{0, 0, 0, 0};
-
-    // Steps of this thread's outputs (n = n0 + tid % 32, m = tid / 32 + 8 q),
-    // fetched before the K loop so the epilogue issues stores only.
-    constexpr int EPT = NR * 16 * FT / 256;  // outputs per thread
-    const int n_own = n0 + (tid & 31);
+    // Steps of this thread's outputs, fetched before the loop so the epilogue
+    // issues stores only (and so they are older than every ring load).
+    constexpr int EPT = NR * 16 * FT / 256;
+    const int n_own = n0 + (tid % NR);
     const float w_own = p.ws[n_own < N ? n_own : N - 1];
     float x_own[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-        const int m = (tid >> 5) + 8 * q;
+        const int m = tid / NR + (256 / NR) * q;
         x_own[q] = p.xs[p.xs_per_row ? (m < M ? m : M - 1) : 0];
     }
 
-    const int steps = (K + 63) / 64;
-    const int per = (steps + 3) / 4;
-    const int s0 = wave * per;
-    const int s1 = s0 + per < steps ? s0 + per : steps;
-    constexpr int U = 4;
-    int s = s0;
-    for (; s + U <= s1; s += U) {
-        int4v a[U][2], b[U][FT];
+    // This wave's stages [s0, s0 + n), wave-uniform.
+    const int nst = (K + 64 * U - 1) / (64 * U);
+    const int per = (nst + 3) / 4;
+    const int waveu = __builtin_amdgcn_readfirstlane(wave);
+    const int s0 = waveu * per;
+    const int n = (s0 + per < nst ? s0 + per : nst) - s0;
+    const uint32_t ring = (uint32_t)(uintptr_t)(lds_void_t *)smem + (uint32_t)(waveu * RING);
+
+    auto issue = [&](int t) {  // stage s0 + t into slot t % S
+        const int off = (s0 + t) * 64 * U;
+        const uint32_t slot = ring + (uint32_t)((t % S) * SLOT);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = (s + u) * 64;
-            const bool ok = k + kg < K;
-            const int kk = ok ? k : -kg;  // past the tail: load chunk 0, zero it
+            // A chunk at or past K is not loaded: the lane re-reads the
+            // row's first 16 bytes and the reader masks that chunk to zero.
+            const int o = off + coff[u] < K ? off + coff[u] : 0;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const int4v v = *reinterpret_cast<const int4v *>(wrow[f] + kk);
-                a[u][f] = ok ? v : int4v{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int t = 0; t < FT; ++t) {
-                const int4v v = *reinterpret_cast<const int4v *>(xrow[t] + kk);
-                b[u][t] = ok ? v : int4v{0, 0, 0, 0};
+            for (int j = 0; j < NFR; ++j) {
+                if (NT && j < NF) lds_dma16_nt(src[j][u] + o, slot + (uint32_t)((j * U + u) * 1024));
+                else lds_dma16(src[j][u] + o, slot + (uint32_t)((j * U + u) * 1024));
             }
         }
+    };
+
+    int4v acc[NF][FT];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int t = 0; t < FT; ++t)
-                    acc[f][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][f], b[u][t],
-                                                                       acc[f][t], 0, 0, 0);
-    }
-    for (; s < s1; ++s) {
-        const int k = s * 64;
-        const bool ok = k + kg < K;
-        const int kk = ok ? k : -kg;
-        int4v a[2], b[FT];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const int4v v = *reinterpret_cast<const int4v *>(wrow[f] + kk);
-            a[f] = ok ? v : int4v{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int t = 0; t < FT; ++t) {
-            const int4v v = *reinterpret_cast<const int4v *>(xrow[t] + kk);
-            b[t] = ok ? v : int4v{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int t = 0; t < FT; ++t)
-                acc[f][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b[t], acc[f][t], 0, 0, 0);
-    }
+        for (int t = 0; t < FT; ++t) acc[f][t] = int4v{0, 0, 0, 0};
+
+    // Reader side: lane (g = lane / 16, i = lane % 16) takes row i, chunk
+    // 4 s + g of step s.
+    const int ri = lane & 15, rg = lane >> 4;
+    const int fi = dec_swz<U>(ri);
+    const char *smem_w = smem + waveu * RING + ri * (64 * U);
 
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int t = 0; t < S - 1; ++t)
+        if (t < n) issue(t);
+    for (int t = 0; t < n; ++t) {
+        // Stage t has landed once at most min(S - 2, n - 1 - t) later stages
+        // are still in flight (loads complete in order).
+        wait_stages<S - 2, P>(n - 1 - t);
+        if (t + S - 1 < n) {
+            // Slot (t - 1) % S is refilled: its LDS reads must be done.
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue(t + S - 1);
+        }
+        const char *sb = smem_w + (t % S) * SLOT;
+        const int off = (s0 + t) * 64 * U;
+#pragma unroll
+        for (int st = 0; st < U; ++st) {
+            const int c = 4 * st + rg;
+            const bool ok = off + 16 * c < K;
+            const int pos = 16 * (c ^ fi);
+            int4v a[NF], b[FT];
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int4v v = *reinterpret_cast<const int4v *>(sb + f * U * 1024 + pos);
+                a[f] = ok ? v : int4v{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int x = 0; x < FT; ++x)
+                b[x] = *reinterpret_cast<const int4v *>(sb + (NF + x) * U * 1024 + pos);
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int x = 0; x < FT; ++x)
+                    acc[f][x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b[x], acc[f][x], 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with its ring: reuse it for the sums
+
+    int *red = reinterpret_cast<int *>(smem);  // [wave][f][t][v * 64 + lane]
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int t = 0; t < FT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) red[wave][f][t][v * 64 + lane] = acc[f][t][v];
+            for (int v = 0; v < 4; ++v)
+                red[((wave * NF + f) * FT + t) * 256 + v * 64 + lane] = acc[f][t][v];
     __syncthreads();
 
-    // 16x16 accumulator layout: lane l, register v holds MFMA row
-    // 4*(l/16) + v (a weight row) and column l%16 (a token).  Threads take
-    // outputs with n fastest so stores of a token row are contiguous.
+    // 16x16 accumulator layout: lane l, register v holds weight row
+    // 4*(l/16) + v and token l%16.  Threads take outputs with n fastest so
+    // the stores of a token row are contiguous.
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
         const int e = tid + 256 * q;
         const int nl = e % NR, ml = e / NR;
-        const int m = ml, n = n0 + nl;
-        if (m >= M || n >= N) continue;
+        const int m = ml, nn = n0 + nl;
+        if (m >= M || nn >= N) continue;
         const int f = nl >> 4, i = nl & 15, t = ml >> 4, j = ml & 15;
         const int l = (i >> 2) * 16 + j, v = i & 3;
-        const int a = red[0][f][t][v * 64 + l] + red[1][f][t][v * 64 + l] +
-                      red[2][f][t][v * 64 + l] + red[3][f][t][v * 64 + l];
-        const float c = x_own[q] * w_own;
-        const int64_t o = (int64_t)m * N + n;
-        store_y<YDT>(p.y, o, (float)a * c);
+        int a = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) a += red[((w * NF + f) * FT + t) * 256 + v * 64 + l];
+        const float cs = x_own[q] * w_own;
+        const int64_t o = (int64_t)m * N + nn;
+        store_y<YDT>(p.y, o, (float)a * cs);
         if (p.acc_out) p.acc_out[o] = a;
     }
 }
@@ -756,22 +873,22 @@ static void launch_tile_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     else gemm_tile<BM, BN, WM, WN, BF16, SIDE><<<grid, block, 0, stream>>>(a);
 }
 
-template <int BM, int BN, int WM, int WN, int ST, bool SIDE>
+template <int BM, int BN, int WM, int WN, int STA, int STB, bool SIDE>
 static void launch_pipe_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
     a.tiles_n = tn;
-    dim3 grid((unsigned)(tm * tn)), block(256);
-    if (y_dt == F32) gemm_pp<BM, BN, WM, WN, ST, F32, SIDE><<<grid, block, 0, stream>>>(a);
-    else if (y_dt == F16) gemm_pp<BM, BN, WM, WN, ST, F16, SIDE><<<grid, block, 0, stream>>>(a);
-    else gemm_pp<BM, BN, WM, WN, ST, BF16, SIDE><<<grid, block, 0, stream>>>(a);
+    dim3 grid((unsigned)(tm * tn)), block(64 * WM * WN);
+    if (y_dt == F32) gemm_pp<BM, BN, WM, WN, STA, STB, F32, SIDE><<<grid, block, 0, stream>>>(a);
+    else if (y_dt == F16) gemm_pp<BM, BN, WM, WN, STA, STB, F16, SIDE><<<grid, block, 0, stream>>>(a);
+    else gemm_pp<BM, BN, WM, WN, STA, STB, BF16, SIDE><<<grid, block, 0, stream>>>(a);
 }
 
-template <int FT>
-static void launch_skinny_t(GemmArgs &a, int y_dt, hipStream_t stream) {
-    dim3 grid((unsigned)((a.N + 31) / 32)), block(256);
-    if (y_dt == F32) gemm_skinny<FT, F32><<<grid, block, 0, stream>>>(a);
-    else if (y_dt == F16) gemm_skinny<FT, F16><<<grid, block, 0, stream>>>(a);
-    else gemm_skinny<FT, BF16><<<grid, block, 0, stream>>>(a);
+template <int NF, int FT, int U, int S, bool NT>
+static void launch_dec_t(GemmArgs &a, int y_dt, hipStream_t stream) {
+    dim3 grid((unsigned)((a.N + 16 * NF - 1) / (16 * NF))), block(256);
+    if (y_dt == F32) gemm_dec<NF, FT, U, S, F32, NT><<<grid, block, 0, stream>>>(a);
+    else if (y_dt == F16) gemm_dec<NF, FT, U, S, F16, NT><<<grid, block, 0, stream>>>(a);
+    else gemm_dec<NF, FT, U, S, BF16, NT><<<grid, block, 0, stream>>>(a);
 }
 
 // Tile shape: the candidate whose tiles fill the 256 CUs best, weighted by
@@ -801,12 +918,22 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     const bool pipe = K % 128 == 0;
     if (side) {
         a.x16 = side->x16; a.w16 = side->w16; a.idx = side->idx; a.count = side->count;
-        if (pipe) launch_pipe_t<128, 128, 2, 2, 2, true>(a, y_dt, stream);
+        if (pipe) launch_pipe_t<128, 128, 2, 2, 2, 2, true>(a, y_dt, stream);
         else launch_tile_t<128, 128, 2, 2, true>(a, y_dt, stream);
         return;
     }
-    if (M <= 16) { launch_skinny_t<1>(a, y_dt, stream); return; }
-    if (M <= 32) { launch_skinny_t<2>(a, y_dt, stream); return; }
+    if (M <= 32) {
+        // Weight rows per block and ring shape by token count: more rows
+        // per block as M grows (each block re-reads all M token rows), two
+        // 64-byte K steps a stage so that a stage covers whole 128-byte
+        // lines of every row (the nontemporal weight stream then fetches
+        // each line once).
+        if (M <= 8) launch_dec_t<1, 1, 2, 4, true>(a, y_dt, stream);
+        else if (M <= 16) launch_dec_t<4, 1, 2, 2, true>(a, y_dt, stream);
+        else if (M <= 24) launch_dec_t<2, 2, 2, 2, true>(a, y_dt, stream);
+        else launch_dec_t<4, 2, 2, 2, true>(a, y_dt, stream);
+        return;
+    }
     // SQ_GEMM_TILE=0|1|2 forces a tile shape (for coverage of every shape).
     int tile = pick_tile(M, N);
     if (const char *e = getenv("SQ_GEMM_TILE")) {
@@ -814,9 +941,9 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     }
     if (pipe) {
         switch (tile) {
-            case 0: launch_pipe_t<256, 256, 2, 2, 2, false>(a, y_dt, stream); break;
-            case 1: launch_pipe_t<256, 128, 2, 2, 3, false>(a, y_dt, stream); break;
-            default: launch_pipe_t<128, 128, 2, 2, 2, false>(a, y_dt, stream); break;
+            case 0: launch_pipe_t<256, 256, 4, 2, 2, 2, false>(a, y_dt, stream); break;
+            case 1: launch_pipe_t<256, 128, 4, 2, 3, 3, false>(a, y_dt, stream); break;
+            default: launch_pipe_t<128, 128, 2, 2, 2, 2, false>(a, y_dt, stream); break;
         }
         return;
     }

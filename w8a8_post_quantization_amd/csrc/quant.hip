@@ -114,25 +114,31 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
     const int64_t nvec = K / V;
     const float inv_static = DYN ? 0.0f : static_scale[1];
 
-    for (int rw = 0; rw < rows_per_wave; ++rw) {
-        const int64_t r = ((int64_t)blockIdx.x * rows_per_wave + rw) * 4 + wave;
-        if (r >= rows) break;
-        const uint4 *xr = x + r * nvec;
-        int8_t *qr = q + r * K;
-        if constexpr (DYN && ITS > 0) {
-            uint4 buf[ITS];
+    // Rows of this wave: ((block * rows_per_wave + i) * 4 + wave).  The wave
+    // index is made explicitly uniform so row bounds become scalar branches.
+    const int64_t wv = __builtin_amdgcn_readfirstlane(wave);
+    auto row_of = [&](int i) { return ((int64_t)blockIdx.x * rows_per_wave + i) * 4 + wv; };
+
+    if constexpr (DYN && ITS > 0) {
+        // Two rows in flight per wave: row i + 1's loads are issued before
+        // row i's stores, so waiting for them never waits for those stores
+        // (vector memory operations complete in issue order).
+        auto load_row = [&](int64_t r, uint4 (&b)[ITS]) {
+            const uint4 *xr = x + r * nvec;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
-                buf[it] = xr[vi < nvec ? vi : nvec - 1];
+                b[it] = ld_nt(xr + (vi < nvec ? vi : nvec - 1));
             }
+        };
+        auto finish_row = [&](int64_t r, const uint4 (&b)[ITS]) {
             float a = 0.0f;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
                 const int64_t vc = vi < nvec ? vi : nvec - 1;
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS>(buf[it], mul, vc * V, v);
+                scaled<DT, HAS_MUL, MUL_LDS>(b[it], mul, vc * V, v);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
@@ -140,16 +146,48 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             if (!(a > 1e-8f)) a = 1e-8f;
             const float inv = 127.0f / a;
             if (lane == 0) scale[r] = a / 127.0f;
+            int8_t *qr = q + r * K;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
+                // Recompute the scaled values from the raw row rather than
+                // keep ITS*V floats alive across the reduction (which would
+                // not fit next to a second row in flight).
+                uint4 raw = b[it];
+                asm volatile("" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.w));
                 const int64_t vi = lane + (int64_t)it * kWave;
                 if (vi < nvec) {
                     float v[V];
-                    scaled<DT, HAS_MUL, MUL_LDS>(buf[it], mul, vi * V, v);
+                    scaled<DT, HAS_MUL, MUL_LDS>(raw, mul, vi * V, v);
                     store_q<DT>(qr, vi * V, v, inv);
                 }
             }
-        } else if constexpr (DYN) {
+        };
+        uint4 b0[ITS], b1[ITS];
+        int64_t r0 = row_of(0);
+        if (r0 >= rows) return;
+        load_row(r0, b0);
+        for (int i = 0;; i += 2) {
+            const int64_t r1 = row_of(i + 1);
+            const bool h1 = i + 1 < rows_per_wave && r1 < rows;
+            if (h1) load_row(r1, b1);
+            finish_row(r0, b0);
+            if (!h1) break;
+            const int64_t r2 = row_of(i + 2);
+            const bool h2 = i + 2 < rows_per_wave && r2 < rows;
+            if (h2) load_row(r2, b0);
+            finish_row(r1, b1);
+            if (!h2) break;
+            r0 = r2;
+        }
+        return;
+    }
+
+    for (int rw = 0; rw < rows_per_wave; ++rw) {
+        const int64_t r = row_of(rw);
+        if (r >= rows) break;
+        const uint4 *xr = x + r * nvec;
+        int8_t *qr = q + r * K;
+        if constexpr (DYN) {
             float a = 0.0f;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];

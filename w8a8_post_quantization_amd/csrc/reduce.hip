@@ -43,8 +43,8 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
         const uint4 *p = x + cv;
         int64_t r = r0 + wave;
         for (; r + 12 < r1; r += 16) {
-            uint4 v0 = p[r * cvec], v1 = p[(r + 4) * cvec];
-            uint4 v2 = p[(r + 8) * cvec], v3 = p[(r + 12) * cvec];
+            uint4 v0 = ld_nt(p + r * cvec), v1 = ld_nt(p + (r + 4) * cvec);
+            uint4 v2 = ld_nt(p + (r + 8) * cvec), v3 = ld_nt(p + (r + 12) * cvec);
             float f[V];
             widen16<DT>(v0, f);
 #pragma unroll
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
         }
         for (; r < r1; r += 4) {
             float f[V];
-            widen16<DT>(p[r * cvec], f);
+            widen16<DT>(ld_nt(p + r * cvec), f);
 #pragma unroll
             for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
         }

@@ -42,6 +42,16 @@ __device__ __forceinline__ void widen16(const uint4 &v, float *out) {
     }
 }
 
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the nontemporal hint, for data each kernel reads once
+// (streamed weights and activations): it keeps the streams from displacing
+// reused data in the caches and measurably raises the sustained HBM read rate.
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+    const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
