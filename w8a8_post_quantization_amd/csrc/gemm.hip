@@ -58,6 +58,51 @@ struct GemmArgs {
     int tiles_n;
 };
 
+// Stage outlier columns t0 .. t0 + tn - 1 (tn <= 32) of the tile's 16-bit
+// activation rows and weight rows into LDS as floats: xo[r * 33 + t],
+// wo[r * 33 + t], zero for t >= tn.  NT threads; thread tid always serves
+// slot t = tid % 32, so it loads its column index once, and its gathers are
+// unconditional (a clamped column for t >= tn, masked when written): a load
+// under a lane-divergent branch would wait for every earlier load.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *wo, int m0,
+                                           int n0, int t0, int tn) {
+    static_assert(NT % 32 == 0 && (BM * 32) % NT == 0 && (BN * 32) % NT == 0, "side staging");
+    constexpr int RX = BM * 32 / NT, RW = BN * 32 / NT;
+    const int tid = threadIdx.x, t = tid & 31, r0 = tid >> 5;
+    const bool live = t < tn;
+    const int64_t col = p.idx[t0 + (live ? t : 0)];
+    // Groups of up to 8 gathers in flight (registers: value and address).
+    constexpr int G = 8;
+    static_assert(RX % G == 0 && RW % G == 0, "gather groups");
+#pragma unroll
+    for (int k0 = 0; k0 < RX; k0 += G) {
+        float v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int r = r0 + (k0 + k) * (NT / 32);
+            const int gr = m0 + r < p.M ? m0 + r : p.M - 1;
+            v[k] = h2f(p.x16[(int64_t)gr * p.K + col]);
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            xo[(r0 + (k0 + k) * (NT / 32)) * 33 + t] = live ? v[k] : 0.0f;
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < RW; k0 += G) {
+        float v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int r = r0 + (k0 + k) * (NT / 32);
+            const int gr = n0 + r < p.N ? n0 + r : p.N - 1;
+            v[k] = h2f(p.w16[(int64_t)gr * p.K + col]);
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            wo[(r0 + (k0 + k) * (NT / 32)) * 33 + t] = live ? v[k] : 0.0f;
+    }
+}
+
 // Each thread fetches (at most) one row step and one column step at kernel
 // start; they are written to LDS only after the main loop, when the loads
 // have long completed.
@@ -104,7 +149,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int fr = lane & 31, fh = lane >> 5;
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = p.M, N = p.N;
     float dw[FN];
     int ncol[FN];
 #pragma unroll
@@ -126,16 +171,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            for (int e = tid; e < BM * 32; e += 256) {
-                const int r = e >> 5, t = e & 31;
-                const int gr = m0 + r < M ? m0 + r : M - 1;
-                xo[r * 33 + t] = t < tn ? h2f(p.x16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
-            }
-            for (int e = tid; e < BN * 32; e += 256) {
-                const int r = e >> 5, t = e & 31;
-                const int gr = n0 + r < N ? n0 + r : N - 1;
-                wo[r * 33 + t] = t < tn ? h2f(p.w16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
-            }
+            stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn);
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -348,27 +384,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Vector store of 4 consecutive outputs (8 bytes for 16-bit types, 16 for
-// fp32), narrowed with round-to-nearest-even.
-template <int YDT>
-__device__ __forceinline__ void store_y4(void *y, int64_t i, const float *v) {
-    if constexpr (YDT == F32) {
-        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + i) =
-            make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-        using T = typename OutT<YDT>::T;
-        T h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = narrow<YDT>(v[q]);
-        *reinterpret_cast<uint2 *>(reinterpret_cast<T *>(y) + i) = __builtin_bit_cast(uint2, h);
-    }
-}
 
-// Epilogue of the K % 64 == 0 kernel.  The MFMAs there take weight rows as
+// Epilogue of the pipelined kernel.  The MFMAs there take weight rows as
 // the A operand and tokens as B, so lane l, register v of fragment (i, j)
 // holds output column n = 8*(v/4) + 4*(l/32) + (v%4) of n-fragment i and
 // row m = l%32 of m-fragment j: four consecutive columns of one row per
-// group of four registers, stored as one 8- or 16-byte vector.
+// group of four registers.
 template <int BM, int BN, int WM, int WN, int YDT, bool SIDE>
 __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                                             int16v (&acc)[BN / WN / 32][BM / WM / 32],
@@ -380,9 +401,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int fr = lane & 31, fh = lane >> 5;
-    const int M = p.M, N = p.N, K = p.K;
-    const bool vec_y = (N & 3) == 0 && ((uintptr_t)p.y & 15) == 0;
-    const bool vec_a = (N & 3) == 0 && ((uintptr_t)p.acc_out & 15) == 0;
+    const int M = p.M, N = p.N;
     float side[SIDE ? FN : 1][SIDE ? FM : 1][16];
     if constexpr (SIDE) {
 #pragma unroll
@@ -397,16 +416,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            for (int e = tid; e < BM * 32; e += NT) {
-                const int r = e >> 5, t = e & 31;
-                const int gr = m0 + r < M ? m0 + r : M - 1;
-                xo[r * 33 + t] = t < tn ? h2f(p.x16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
-            }
-            for (int e = tid; e < BN * 32; e += NT) {
-                const int r = e >> 5, t = e & 31;
-                const int gr = n0 + r < N ? n0 + r : N - 1;
-                wo[r * 33 + t] = t < tn ? h2f(p.w16[(int64_t)gr * K + p.idx[t0 + t]]) : 0.0f;
-            }
+            stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn);
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < FN; ++i)
@@ -425,50 +435,121 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                     }
         }
     }
+    // Exact int32 sums, when asked for (direct stores, not on the fast path).
+    if (p.acc_out) {
+        const bool vec_a = (N & 3) == 0 && ((uintptr_t)p.acc_out & 15) == 0;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wm * WTM + j * 32 + fr;
+            if (m >= M) continue;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fh;
+                    const int64_t o = (int64_t)m * N + n;
+                    if (vec_a && n + 3 < N) {
+                        *reinterpret_cast<int4 *>(p.acc_out + o) =
+                            make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < N) p.acc_out[o + q] = acc[i][j][4 * g + q];
+                    }
+                }
+        }
+    }
+
+    if constexpr (SIDE) {
+        // Final values y = fl(fl(acc) * c) + side, folded into the side
+        // array now so the accumulators are dead before the slab stores.
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const float dx = sx[wm * WTM + j * 32 + fr];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 dw4 =
+                        *reinterpret_cast<const float4 *>(sw + wn * WTN + i * 32 + 8 * g + 4 * fh);
+                    const float dwq[4] = {dw4.x, dw4.y, dw4.z, dw4.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float c = dx * dwq[q];
+                        const float deq = (float)acc[i][j][4 * g + q] * c;
+                        side[i][j][4 * g + q] = deq + side[i][j][4 * g + q];
+                    }
+                }
+        }
+        __syncthreads();  // the ring held the side operands
+    }
+
+    // Outputs go through a wave-private slab of the (now free) ring: 32 rows
+    // x WTN columns of the output type per m-fragment, written from the
+    // accumulator layout and read back 16 bytes per lane along rows, so a
+    // quarter-wave stores 128-256 contiguous bytes instead of touching 16
+    // rows.  16-byte chunk c of slab row r sits at position c ^ f(r).
+    using T = typename OutT<YDT>::T;
+    constexpr int RB = WTN * (int)sizeof(T);       // slab row bytes
+    constexpr int CPR = RB / 16;                   // 16-byte chunks per row
+    constexpr int RPW = RB >= 256 ? 1 : 256 / RB;  // rows per 256-byte bank window
+    constexpr int EPC = 16 / (int)sizeof(T);       // outputs per chunk
+    static_assert(RB % 16 == 0 && WM * WN * 32 * RB <= (BM + BN) * 128 * 2, "slab");
+    int8_t *slab = smem + wave * (32 * RB);
+    const bool vec_y = ((N * (int)sizeof(T)) & 15) == 0 && ((uintptr_t)p.y & 15) == 0;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + j * 32 + fr;
-        const int m = m0 + ml;
         const float dx = sx[ml];
+        const int fw = (fr / RPW) & (CPR - 1);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int nl = wn * WTN + i * 32 + 8 * g + 4 * fh;
-                const int n = n0 + nl;
-                const float4 dw4 = *reinterpret_cast<const float4 *>(sw + nl);
+                const int cl = i * 32 + 8 * g + 4 * fh;  // first of 4 columns in the wave tile
+                const float4 dw4 = *reinterpret_cast<const float4 *>(sw + wn * WTN + cl);
                 const float dwq[4] = {dw4.x, dw4.y, dw4.z, dw4.w};
-                float yv[4];
+                T h[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float c = dx * dwq[q];
-                    const float deq = (float)acc[i][j][4 * g + q] * c;
-                    if constexpr (SIDE) yv[q] = deq + side[i][j][4 * g + q];
-                    else yv[q] = deq;
-                }
-                if (m < M) {
-                    const int64_t o = (int64_t)m * N + n;
-                    if (vec_y && n + 3 < N) {
-                        store_y4<YDT>(p.y, o, yv);
+                    if constexpr (SIDE) {
+                        h[q] = narrow<YDT>(side[i][j][4 * g + q]);
                     } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (n + q < N) store_y<YDT>(p.y, o + q, yv[q]);
-                    }
-                    if (p.acc_out) {
-                        if (vec_a && n + 3 < N) {
-                            *reinterpret_cast<int4 *>(p.acc_out + o) =
-                                make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                          acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                if (n + q < N) p.acc_out[o + q] = acc[i][j][4 * g + q];
-                        }
+                        const float c = dx * dwq[q];
+                        h[q] = narrow<YDT>((float)acc[i][j][4 * g + q] * c);
                     }
                 }
+                const int cb = cl * (int)sizeof(T);  // byte offset in the slab row
+                int8_t *dst = slab + fr * RB + (((cb >> 4) ^ fw) << 4) + (cb & 15);
+                if constexpr (sizeof(T) == 4) *reinterpret_cast<uint4 *>(dst) = __builtin_bit_cast(uint4, h);
+                else *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, h);
             }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab written (one wave)
+        static_assert((32 * CPR) % 64 == 0, "slab chunks per lane");
+#pragma unroll
+        for (int k = 0; k < 32 * CPR / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int r = c / CPR, ch = c % CPR;
+            const uint4 v = *reinterpret_cast<const uint4 *>(
+                slab + r * RB + ((ch ^ ((r / RPW) & (CPR - 1))) << 4));
+            const int m = m0 + wm * WTM + j * 32 + r;
+            const int n = n0 + wn * WTN + ch * EPC;
+            if (m >= M || n >= N) continue;
+            T *yp = reinterpret_cast<T *>(p.y) + (int64_t)m * N + n;
+            if (vec_y && n + EPC <= N) {
+                *reinterpret_cast<uint4 *>(yp) = v;
+            } else {
+                T e[EPC];
+                __builtin_memcpy(e, &v, 16);
+#pragma unroll
+                for (int q = 0; q < EPC; ++q)
+                    if (n + q < N) yp[q] = e[q];
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab read before reuse
     }
+
 }
 
 // Scheduling pattern after the stage barrier: each MFMA is followed by one
@@ -495,20 +576,22 @@ __device__ __forceinline__ void sched_tail() {
 // writes LDS bytes [16 l, 16 l + 16) of its 1 KiB block; the swizzle (see
 // swz) is applied by choosing which global chunk each lane fetches.
 //
-// The rings differ in depth because the operands differ in latency: the
-// activation tile is re-read by every block from L2, while each weight byte
-// comes once from HBM, so weights are prefetched STB - 1 stages ahead
-// (about 2 us at full MFMA rate when STB = 5) and activations one stage.
-// Loads complete in issue order; per iteration the kernel issues the
+// The rings may differ in depth (STB > STA = 2 prefetches weights further
+// ahead than activations), but loads complete in issue order, so waiting
+// for activation stage kt + 1 also waits for every weight stage issued
+// before it: a deeper weight ring buys no latency.  The shapes used run
+// both rings in lockstep (STB == STA).  Per iteration the kernel issues the
 // activation stage kt + STA, then the weight stage kt + STB, which fixes
-// the vmcnt values below.  With STB == STA the rings move in lockstep.
+// the vmcnt values below.
 //
 // Each stage is consumed as four 32-byte quarters with ping-pong fragment
 // registers: a quarter's LDS reads overlap the previous quarter's MFMAs, and
 // after the stage barrier the next stage's first reads overlap the last
 // quarter's MFMAs.  Weight rows are the MFMA A operand (see epilogue_nt).
+// The side-term variant asks for two waves per SIMD: its 128x128 tiles are
+// small, and one wave per SIMD halves how many tiles a CU has in flight.
 template <int BM, int BN, int WM, int WN, int STA, int STB, int YDT, bool SIDE>
-__global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(1, 4))) void
+__global__ __launch_bounds__(64 * WM * WN, SIDE ? 2 : 1) __attribute__((amdgpu_waves_per_eu(SIDE ? 2 : 1, 4))) void
 gemm_pp(GemmArgs p) {
     constexpr int BK = 128;
     constexpr int NW = WM * WN;  // waves

@@ -14,9 +14,10 @@
 //    exact and by 0.0 gives +-0, which quantizes to 0, the same as
 //    removing the column.
 //
-// One 64-lane wave per row.  Each lane keeps its 16-byte vectors of the row
-// in registers (up to 16 per lane: 8192 16-bit or 4096 fp32 elements), so
-// HBM is read once and written once; longer rows re-read from L2.
+// One 64-lane wave per row (or, for few rows, one 256-thread block per
+// row).  Each lane keeps its 16-byte vectors of the row in registers (up to
+// 16 per lane: 8192 16-bit or 4096 fp32 elements), so HBM is read once and
+// written once; longer rows re-read from L2.
 #include "sq_device.h"
 #include "sq_launch.h"
 
@@ -214,9 +215,93 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
     }
 }
 
+// Few rows (fewer than the chip's wave slots): one 256-thread block per row,
+// ITS 16-byte vectors per thread, all loads (row and multiplier) issued
+// before the reduction; the row maximum is combined across the 4 waves
+// through LDS.  Out-of-range vector indices are clamped to the row's last
+// vector (loaded, not used) so every load is unconditional.
+template <int DT, bool HAS_MUL, bool DYN, int ITS>
+__global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__restrict__ x,
+                                                              int64_t K,
+                                                              const float *__restrict__ mul,
+                                                              const float *__restrict__ static_scale,
+                                                              int8_t *__restrict__ q,
+                                                              float *__restrict__ scale) {
+    constexpr int V = Vec<DT>::n;
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = blockIdx.x;
+    if (!DYN && r == 0 && tid == 0) scale[0] = static_scale[0];
+    const int64_t nvec = K / V;
+    const uint4 *xr = x + r * nvec;
+    uint4 raw[ITS];
+    float m[HAS_MUL ? ITS : 1][HAS_MUL ? V : 1];
+#pragma unroll
+    for (int it = 0; it < ITS; ++it) {
+        const int64_t vi = tid + (int64_t)it * 256;
+        const int64_t vc = vi < nvec ? vi : nvec - 1;
+        raw[it] = ld_nt(xr + vc);
+        if constexpr (HAS_MUL) load_mul<DT>(mul, vc * V, m[it]);
+    }
+    float inv;
+    if constexpr (DYN) {
+        float a = 0.0f;
+#pragma unroll
+        for (int it = 0; it < ITS; ++it) {
+            const int64_t vi = tid + (int64_t)it * 256;
+            float v[V];
+            widen16<DT>(raw[it], v);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if constexpr (HAS_MUL) v[i] = v[i] * m[it][i];
+                if (vi < nvec) a = fmaxf(a, fabsf(v[i]));
+            }
+        }
+        a = wave_max(a);
+        if (lane == 0) wmax[wave] = a;
+        __syncthreads();
+        a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        if (!(a > 1e-8f)) a = 1e-8f;
+        inv = 127.0f / a;
+        if (tid == 0) scale[r] = a / 127.0f;
+    } else {
+        inv = static_scale[1];
+    }
+    int8_t *qr = q + r * K;
+#pragma unroll
+    for (int it = 0; it < ITS; ++it) {
+        const int64_t vi = tid + (int64_t)it * 256;
+        if (vi < nvec) {
+            float v[V];
+            widen16<DT>(raw[it], v);
+            if constexpr (HAS_MUL) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) v[i] = v[i] * m[it][i];
+            }
+            store_q<DT>(qr, vi * V, v, inv);
+        }
+    }
+}
+
 template <int DT, bool HAS_MUL, bool DYN>
 static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream) {
+    auto *xv = reinterpret_cast<const uint4 *>(x);
+    const int64_t nvec = K / Vec<DT>::n;
+    // Fewer rows than ~2 waves per SIMD of the chip, and long enough rows:
+    // a block per row.
+    if (rows < 2048 && nvec >= 256 && nvec <= 8 * 256) {
+        const int64_t its = (nvec + 255) / 256;
+        dim3 grid((unsigned)rows), block(256);
+#define SQ_B(ITS) \
+    quant_row_block_kernel<DT, HAS_MUL, DYN, ITS><<<grid, block, 0, stream>>>(xv, K, mul, static_scale, q, scale)
+        if (its <= 1) SQ_B(1);
+        else if (its <= 2) SQ_B(2);
+        else if (its <= 4) SQ_B(4);
+        else SQ_B(8);
+#undef SQ_B
+        return;
+    }
     // Rows per wave: enough blocks to fill the chip (>= ~1024), more rows
     // per block when there are plenty, so the multiplier is staged rarely.
     int64_t rpw = rows / (4 * 1024);
@@ -226,8 +311,7 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     const bool mul_lds = HAS_MUL && K <= kMulLds;
     const size_t shmem = mul_lds ? (size_t)K * sizeof(float) : 0;
     dim3 grid((unsigned)blocks), block(256);
-    auto *xv = reinterpret_cast<const uint4 *>(x);
-    const int64_t nit = (K / Vec<DT>::n + kWave - 1) / kWave;  // vectors per lane
+    const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
 #define SQ_Q(ITS, LDS)                                                                     \
     quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS><<<grid, block, shmem, stream>>>(         \

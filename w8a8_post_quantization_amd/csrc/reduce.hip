@@ -3,11 +3,11 @@
 // absmax_cols: per-channel abs-max of a row-major [rows, cols] matrix
 // ("x_j = max_i |X_ij|" and the weight-side w_j of the SmoothQuant tutorial
 // page, section 缩放因子; the calibration code of the lpnh.cn write-up §3.2).
-// Each lane owns one 16-byte column vector and keeps a running max over a
-// strided slab of rows; a block folds its four waves through LDS and merges
-// into the output with one atomicMax per column on the float bit pattern
-// (non-negative floats order like their unsigned bits).  Reads are
-// coalesced 1 KiB row segments per wave; the kernel is HBM-bound.
+// Each thread owns one 16-byte column vector and keeps a running max over a
+// strided slab of rows; a block folds its 16 row groups through LDS and
+// merges into the output with one atomicMax per column on the float bit
+// pattern (non-negative floats order like their unsigned bits).  Reads are
+// coalesced 256-byte row segments; the kernel is HBM-bound.
 //
 // compute_scales: s_j = max(max(x_j,1e-5)^a / max(w_j,1e-5)^(1-a), 1e-5),
 // powers and quotient in double rounded once; inv_s = fl(1/s); optional
@@ -22,16 +22,22 @@ __global__ void fill_zero_u32(uint32_t *p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
+// Block = 16 row groups x 16 column vectors: a wave reads four 256-byte row
+// segments per load, thread (g, c) keeps the max of column vector c over
+// rows r0 + g, r0 + g + 16, ... of the block's slab.
+constexpr int kCvb = 16;           // column vectors per block
+constexpr int kRg = 256 / kCvb;    // row groups per block
+
 template <int DT>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           int64_t rows_per_block,
                                                           uint32_t *__restrict__ out) {
     constexpr int V = Vec<DT>::n;
-    __shared__ float red[4][kWave * V];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ float red[kRg][kCvb * V + 1];
+    const int tid = threadIdx.x, c = tid % kCvb, g = tid / kCvb;
     const int64_t cvec = cols / V;
-    const int64_t cv = (int64_t)blockIdx.x * kWave + lane;
+    const int64_t cv = (int64_t)blockIdx.x * kCvb + c;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
 
@@ -41,10 +47,10 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
 
     if (cv < cvec) {
         const uint4 *p = x + cv;
-        int64_t r = r0 + wave;
-        for (; r + 12 < r1; r += 16) {
-            uint4 v0 = ld_nt(p + r * cvec), v1 = ld_nt(p + (r + 4) * cvec);
-            uint4 v2 = ld_nt(p + (r + 8) * cvec), v3 = ld_nt(p + (r + 12) * cvec);
+        int64_t r = r0 + g;
+        for (; r + 3 * kRg < r1; r += 4 * kRg) {
+            uint4 v0 = ld_nt(p + r * cvec), v1 = ld_nt(p + (r + kRg) * cvec);
+            uint4 v2 = ld_nt(p + (r + 2 * kRg) * cvec), v3 = ld_nt(p + (r + 3 * kRg) * cvec);
             float f[V];
             widen16<DT>(v0, f);
 #pragma unroll
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
 #pragma unroll
             for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
         }
-        for (; r < r1; r += 4) {
+        for (; r < r1; r += kRg) {
             float f[V];
             widen16<DT>(ld_nt(p + r * cvec), f);
 #pragma unroll
@@ -67,13 +73,13 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
         }
     }
 #pragma unroll
-    for (int i = 0; i < V; ++i) red[wave][i * kWave + lane] = m[i];
+    for (int i = 0; i < V; ++i) red[g][c * V + i] = m[i];
     __syncthreads();
-    for (int c = threadIdx.x; c < kWave * V; c += 256) {
-        const float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-        // red[.][i*64 + l] holds column (vector l, element i)
-        const int l = c & 63, i = c >> 6;
-        const int64_t col = ((int64_t)blockIdx.x * kWave + l) * V + i;
+    if (tid < kCvb * V) {
+        float v = red[0][tid];
+#pragma unroll
+        for (int k = 1; k < kRg; ++k) v = fmaxf(v, red[k][tid]);
+        const int64_t col = (int64_t)blockIdx.x * kCvb * V + tid;  // red[.][c*V + i] = column c*V + i
         if (col < cols && v > 0.0f) atomicMax(&out[col], __float_as_uint(v));
     }
 }
@@ -87,8 +93,10 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
     if (rows == 0) return;
     const int V = dt == F32 ? 4 : 8;
     const int64_t cvec = cols / V;
-    const int64_t bx = (cvec + kWave - 1) / kWave;
-    // Aim for ~2048 blocks (8 per CU) with at least 64 rows per block.
+    const int64_t bx = (cvec + kCvb - 1) / kCvb;
+    // Aim for ~2048 blocks (8 per CU) with at least 64 rows per block (4 per
+    // thread): the blocks of one column slab merge with one atomicMax per
+    // column each, so their number is kept small.
     int64_t by = (2048 + bx - 1) / bx;
     const int64_t max_by = (rows + 63) / 64;
     if (by > max_by) by = max_by;
