@@ -94,10 +94,11 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
     const int V = dt == F32 ? 4 : 8;
     const int64_t cvec = cols / V;
     const int64_t bx = (cvec + kCvb - 1) / kCvb;
-    // Aim for ~2048 blocks (8 per CU) with at least 64 rows per block (4 per
-    // thread): the blocks of one column slab merge with one atomicMax per
-    // column each, so their number is kept small.
-    int64_t by = (2048 + bx - 1) / bx;
+    // At most 2048 blocks - one round at 8 blocks per CU, so no block of a
+    // second round streams its slab alone at the end - with at least 64
+    // rows per block (4 per thread): the blocks of one column slab merge
+    // with one atomicMax per column each, so their number is kept small.
+    int64_t by = 2048 / bx;
     const int64_t max_by = (rows + 63) / 64;
     if (by > max_by) by = max_by;
     if (by > 65535) by = 65535;
