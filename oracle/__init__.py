@@ -26,6 +26,7 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
 
 F32, F16, BF16 = 0, 1, 2
 PER_TENSOR_STATIC, PER_TOKEN_DYNAMIC = 0, 1
+NORM_LAYER, NORM_RMS = 0, 1
 _lib = None
 
 _P = ctypes.c_void_p
@@ -72,6 +73,9 @@ def lib():
                                          _I64, _P, _P]),
             "orc_matmul_f64": (None, [_P, _I, _P, _I, _I64, _I64, _I64, _P]),
             "orc_smoothed_matmul_f64": (None, [_P, _I, _P, _I, _P, _I64, _I64, _I64, _P]),
+            "orc_fold_norm": (None, [_P, _P, _P, _I64, _P, _P]),
+            "orc_norm_stats": (None, [_P, _I64, _I64, _I, _F, _P, _P]),
+            "orc_norm_quantize": (None, [_P, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -294,3 +298,47 @@ def f32_to_bf16_bits(v: float) -> int:
 
 def round_half_even(v: float) -> float:
     return lib().orc_round_half_even(v)
+
+
+def _f16_bits(x):
+    x = _c(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16)
+    raise TypeError("fp16 input expected")
+
+
+def fold_norm(gamma, s, beta=None):
+    """gamma' = fl(gamma / s), beta' = fl(beta / s) (the SmoothQuant tutorial
+    page, section on folding into LayerNorm)."""
+    gamma = _c(gamma.astype(np.float32))
+    s = _c(s.astype(np.float32))
+    g_out = np.empty_like(gamma)
+    b = None if beta is None else _c(beta.astype(np.float32))
+    b_out = None if b is None else np.empty_like(b)
+    lib().orc_fold_norm(_ptr(gamma), _ptr(b), _ptr(s), gamma.size, _ptr(g_out), _ptr(b_out))
+    return g_out, b_out
+
+
+def norm_stats(x_f16, norm=NORM_LAYER, eps=1e-5):
+    """Per-row (mu, rstd) in fp32 from exact row sums."""
+    xb = _f16_bits(x_f16)
+    M, K = xb.shape
+    mu, rstd = np.empty(M, np.float32), np.empty(M, np.float32)
+    lib().orc_norm_stats(_ptr(xb), M, K, norm, eps, _ptr(mu), _ptr(rstd))
+    return mu, rstd
+
+
+def norm_quantize(x_f16, gamma, beta=None, norm=NORM_LAYER, eps=1e-5,
+                  mode=PER_TOKEN_DYNAMIC, static_scale=None, want_y=False):
+    """Fused norm -> int8: returns (xq, x_scale) or (xq, x_scale, y fp32)."""
+    xb = _f16_bits(x_f16)
+    M, K = xb.shape
+    gamma = _c(gamma.astype(np.float32))
+    beta = None if beta is None else _c(beta.astype(np.float32))
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M if mode == PER_TOKEN_DYNAMIC else 1, np.float32)
+    st = None if static_scale is None else _c(static_scale.astype(np.float32))
+    y = np.empty((M, K), np.float32) if want_y else None
+    lib().orc_norm_quantize(_ptr(xb), M, K, norm, _ptr(gamma), _ptr(beta), eps, mode,
+                            _ptr(st), _ptr(xq), _ptr(xs), _ptr(y))
+    return (xq, xs, y) if want_y else (xq, xs)

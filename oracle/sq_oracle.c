@@ -399,3 +399,84 @@ void orc_smoothed_matmul_f64(const void *x, int xdt, const void *w, int wdt,
             ys64[m * N + n] = acc;
         }
 }
+
+/* ------------------------------------------- norm folding and fused norm */
+
+void orc_fold_norm(const float *gamma, const float *beta, const float *s,
+                   int64_t K, float *gamma_out, float *beta_out) {
+    for (int64_t j = 0; j < K; ++j) {
+        gamma_out[j] = gamma[j] / s[j];
+        if (beta) beta_out[j] = beta[j] / s[j];
+    }
+}
+
+typedef unsigned __int128 u128;
+
+static double u128_to_double(u128 v) {
+    const uint64_t hi = (uint64_t)(v >> 64), lo = (uint64_t)v;
+    return (double)hi * 18446744073709551616.0 + (double)lo;
+}
+
+static void row_stats(const uint16_t *x, int64_t K, int norm, float eps, float *mu32,
+                      float *rstd32) {
+    int64_t s1 = 0;
+    u128 s2 = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        /* x * 2^24 is an integer below 2^40: exact in double and in int64 */
+        const int64_t xi = (int64_t)((double)orc_f16_to_f32(x[j]) * 16777216.0);
+        const uint64_t a = (uint64_t)(xi < 0 ? -xi : xi);
+        s1 += xi;
+        s2 += (u128)a * a;
+    }
+    const double kd = (double)K;
+    double mu = 0.0, var;
+    if (norm == ORC_NORM_LAYER) {
+        mu = (double)s1 / (kd * 16777216.0);
+        const u128 sq1 = (u128)(s1 < 0 ? -s1 : s1) * (u128)(s1 < 0 ? -s1 : s1);
+        const u128 v = (u128)K * s2 - sq1; /* K S2 >= S1^2 (Cauchy-Schwarz) */
+        var = u128_to_double(v) / (kd * kd * 281474976710656.0);
+    } else {
+        var = u128_to_double(s2) / (kd * 281474976710656.0);
+    }
+    *mu32 = (float)mu;
+    *rstd32 = (float)(1.0 / sqrt(var + (double)eps));
+}
+
+void orc_norm_stats(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
+                    float eps, float *mu, float *rstd) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) row_stats(x_f16 + m * K, K, norm, eps, &mu[m], &rstd[m]);
+}
+
+void orc_norm_quantize(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
+                       const float *gamma, const float *beta, float eps,
+                       int mode, const float *static_scale, int8_t *xq,
+                       float *x_scale, float *y_out) {
+    if (mode == ORC_PER_TENSOR_STATIC) x_scale[0] = static_scale[0];
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            const uint16_t *x = x_f16 + m * K;
+            float mu, rstd;
+            row_stats(x, K, norm, eps, &mu, &rstd);
+            for (int64_t j = 0; j < K; ++j) {
+                const float v = orc_f16_to_f32(x[j]);
+                const float n = norm == ORC_NORM_LAYER ? (v - mu) * rstd : v * rstd;
+                float y = n * gamma[j];
+                if (beta) y = y + beta[j];
+                row[j] = y;
+            }
+            if (y_out) memcpy(y_out + m * K, row, (size_t)K * sizeof(float));
+            if (mode == ORC_PER_TOKEN_DYNAMIC) {
+                quantize_row(row, K, xq + m * K, &x_scale[m]);
+            } else {
+                const float inv = static_scale[1];
+                for (int64_t j = 0; j < K; ++j)
+                    xq[m * K + j] = clamp_i8(orc_round_half_even(row[j] * inv));
+            }
+        }
+        free(row);
+    }
+}

@@ -173,4 +173,53 @@ void orc_smoothed_matmul_f64(const void *x, int xdt, const void *w, int wdt,
                              const float *s, int64_t M, int64_t N, int64_t K,
                              double *ys64);
 
+/* ------------------------------------------------------------------------
+ * Folding the smoothing into the preceding norm, and the fused
+ * norm -> int8 quantizer.
+ *
+ * [SQ-tutorial] section 融入 LayerNorm: the norm before q/k/v (and before
+ * gate/up) computes y_j = (x_j - mu) / sigma * gamma_j + beta_j; dividing
+ * its parameters once, gamma'_j = gamma_j / s_j and beta'_j = beta_j / s_j,
+ * makes it emit y_j / s_j, the smoothed activation a4 would otherwise form.
+ */
+#define ORC_NORM_LAYER 0
+#define ORC_NORM_RMS 1
+
+/* gamma_out[j] = fl(gamma[j] / s[j]); beta_out[j] = fl(beta[j] / s[j]) when
+ * beta != NULL.  Pinned: exact for power-of-two s; the folded norm equals
+ * the unfolded one divided by s within rounding. */
+void orc_fold_norm(const float *gamma, const float *beta, const float *s,
+                   int64_t K, float *gamma_out, float *beta_out);
+
+/* Row statistics of fp16 rows (x_f16 [M, K] raw bits), computed exactly:
+ * every fp16 value times 2^24 is an integer below 2^40, so
+ *   S1 = sum_j x_j 2^24 (int64) and S2 = sum_j (x_j 2^24)^2 (128-bit)
+ * are exact in any order.  Then, in double:
+ *   LAYER: mu = S1 / (K 2^24); var = (K S2 - S1^2) / (K^2 2^48)
+ *          (the population variance, mean of (x - mu)^2, exactly);
+ *   RMS:   mu = 0;           var = S2 / (K 2^48)      (mean of x^2);
+ *   rstd = 1 / sqrt(var + eps);
+ * and mu, rstd rounded to fp32.  The 128-bit integers are converted to
+ * double as fl(hi 2^64 + fl(lo)) (hi, lo the 64-bit halves).
+ * Pinned: mu, var against exact rational arithmetic; rstd against
+ * 1/sqrt in double; invariance of the layer norm under x -> 2x (eps = 0). */
+void orc_norm_stats(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
+                    float eps, float *mu, float *rstd);
+
+/* Fused norm + int8 quantization of fp16 rows.  Per element, in fp32:
+ *   LAYER: y = fl(fl(fl(x - mu) * rstd) * gamma_j)  (+ beta_j, one more fl)
+ *   RMS:   y = fl(fl(x * rstd) * gamma_j)           (+ beta_j if given)
+ * with (mu, rstd) from orc_norm_stats; gamma / beta are the folded
+ * parameters (orc_fold_norm) or the plain ones.  Then, as orc_quantize_act:
+ * PER_TOKEN_DYNAMIC quantizes each row with its own step (x_scale[M]),
+ * PER_TENSOR_STATIC uses static_scale (x_scale[0] = static_scale[0]).
+ * y_out (optional, [M, K] fp32) receives y.  [SQ-tutorial] 融入 LayerNorm
+ * (the norm and its folded parameters) and 为什么激活不能用逐通道量化
+ * (per-token / per-tensor activation quantization).
+ * Pinned: y against the fp64 norm; constant rows give y = beta exactly. */
+void orc_norm_quantize(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
+                       const float *gamma, const float *beta, float eps,
+                       int mode, const float *static_scale, int8_t *xq,
+                       float *x_scale, float *y_out);
+
 #endif
