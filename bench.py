@@ -14,7 +14,8 @@ roofline of the step's dominant kernel, per-kernel times, and separately
 timed kernel-level figures: the prefill GEMM with cold weights (rotating
 copies larger than the 256 MB last-level cache), decode GEMMs at M = 1, 8,
 32 (HBM GB/s), activation quantization and abs-max on a 940 MB stream, the
-LLM.int8() mixed matmul and the hidden-1024 decoder GEMM set.  All inputs
+LLM.int8() mixed matmul, the hidden-1024 decoder GEMM set and the fused
+norm -> int8 quantizer (smoothing folded into the norm).  All inputs
 are seeded synthetic data, generated on the host and resident in HBM before
 any timed region.  `cpu_baseline` times the CPU oracle on a bounded slice
 of the same step on this host.
@@ -57,8 +58,7 @@ def parse():
 # while the kernel's sources still hash to what the counters were taken on.
 TRAFFIC_FILES = {"a3_smooth_weights": "a3_smooth_weights_prefill_30b_traffic.md"}
 KERNEL_SOURCES = {"a3_smooth_weights": ["w8a8_post_quantization_amd/csrc/quant.hip",
-                                        "w8a8_post_quantization_amd/csrc/sq_device.h",
-                                        "w8a8_post_quantization_amd/csrc/sq_launch.h"]}
+                                        "w8a8_post_quantization_amd/csrc/sq_device.h"]}
 
 
 def sources_sha256(kernel):
@@ -359,6 +359,19 @@ def extras(torch, L, _sp, T, chk):
     b = M * K * 2 + 4 * K
     res["absmax_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
                             "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    # Fused norm (smoothing folded into gamma / beta) -> per-token int8 on
+    # the same stream, and on the prefill activations.
+    gam, bet = U(K, 1.0), U(K, 0.1)
+    us = _time_loop(torch, [lambda: chk(L.sq_norm_quantize_act(
+        P(Xs), 1, M, K, 0, P(gam), P(bet), 1e-5, 1, None, P(xq), P(xs), sp), "normq")], 10)
+    b = M * K * 3 + 8 * K + 4 * M
+    res["norm_quant_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                                "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    Mp = 256
+    us = _time_loop(torch, [lambda: chk(L.sq_norm_quantize_act(
+        P(Xs), 1, Mp, K, 0, P(gam), P(bet), 1e-5, 1, None, P(xq), P(xs), sp), "normq")], 50)
+    res["norm_quant_prefill"] = {"us": round(us, 2),
+                                 "GBs": round((Mp * K * 3 + 8 * K + 4 * Mp) / us / 1e3, 1)}
     del Xs, xq
 
     # LLM.int8() mixed matmul, X fp16 [2048, 4096] with 6 planted dims, tau = 6.

@@ -56,6 +56,8 @@ typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
 
 typedef enum { SQ_PER_TENSOR_STATIC = 0, SQ_PER_TOKEN_DYNAMIC = 1 } sq_qmode;
 
+typedef enum { SQ_NORM_LAYER = 0, SQ_NORM_RMS = 1 } sq_norm;
+
 /* Human-readable name of a status code (static string). */
 const char *sq_status_str(int status);
 
@@ -122,6 +124,8 @@ int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
  *   inv_s        [K] fp32 or NULL (no smoothing, e.g. folded upstream)
  *   static_scale [2] fp32 {step, 1/step} (static mode only, else ignored)
  *   xq           [M, K] int8 out; x_scale [M] (dynamic) or [1] (static) out
+ *                (with M == 0 in dynamic mode nothing is written and x_scale
+ *                may be NULL; in static mode x_scale[0] is still set)
  * K % 16 == 0.
  */
 int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
@@ -174,6 +178,44 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
                          float threshold, void *workspace,
                          size_t workspace_bytes, void *y, int y_dt,
                          int32_t *n_outliers_out, void *stream);
+
+/*
+ * Folding the smoothing into the norm that precedes the layer
+ * ([SQ-tutorial] section 融入 LayerNorm: the norm's output times 1/s_j is
+ * obtained by dividing its parameters once).
+ *   gamma, beta  [K] fp32 in (beta may be NULL: no shift)
+ *   s            [K] fp32 smoothing factors (sq_compute_scales)
+ *   gamma_out    [K] fp32 out: fl(gamma_j / s_j)
+ *   beta_out     [K] fp32 out: fl(beta_j / s_j); required iff beta != NULL
+ * Outputs may alias their inputs.  Pointers 4-byte aligned.
+ */
+int sq_fold_norm(const float *gamma, const float *beta, const float *s, int64_t K,
+                 float *gamma_out, float *beta_out, void *stream);
+
+/*
+ * Fused norm + int8 quantization of fp16 rows: the norm of [SQ-tutorial]
+ * 融入 LayerNorm, y_j = (x_j - mu) / sigma * gamma_j + beta_j, with the
+ * folded parameters (sq_fold_norm) it emits the smoothed activation, which
+ * is quantized in the same pass as sq_quantize_act does (per token or per
+ * tensor) - the residual row is read once and only int8 is written.
+ *   x      [M, K] fp16 (dt must be SQ_F16), finite
+ *   norm   SQ_NORM_LAYER: mu = mean_j x_j, sigma^2 = mean_j (x_j - mu)^2;
+ *          SQ_NORM_RMS:   mu = 0,          sigma^2 = mean_j x_j^2
+ *          The sums are exact (every fp16 value times 2^24 is an integer);
+ *          in double: mu = S1 / (K 2^24), sigma^2 from the exact integers,
+ *          rstd = 1 / sqrt(sigma^2 + eps); then mu, rstd rounded to fp32.
+ *   gamma  [K] fp32 (16-byte aligned); beta [K] fp32 or NULL (no shift)
+ *   eps    >= 0, finite
+ *   per element in fp32: n = fl(fl(x - mu) * rstd) (LAYER) or fl(x * rstd)
+ *          (RMS), y = fl(n * gamma_j), then y = fl(y + beta_j) if beta
+ *   mode / static_scale / xq / x_scale: as sq_quantize_act, applied to y
+ * K % 16 == 0, 16 <= K <= 16384 when M > 0 (else SQ_ERR_SHAPE /
+ * SQ_ERR_UNSUPPORTED).
+ */
+int sq_norm_quantize_act(const void *x, int dt, int64_t M, int64_t K, int norm,
+                         const float *gamma, const float *beta, float eps, int mode,
+                         const float *static_scale, int8_t *xq, float *x_scale,
+                         void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,8 @@ Both the GPU path and the CPU oracle receive the very same host arrays.
 
 Workload recipes (stream ids: 1 = X, 2 = W, 3 = outlier channels,
 4 = outlier factors, 5 = outlier row draws, 6 = second/calibration X,
-7 = outlier signs, 8 = outlier magnitudes, 10+i = i-th weight of a layer set):
+7 = outlier signs, 8 = outlier magnitudes, 10+i = i-th weight of a layer set,
+20 = norm gamma, 21 = norm beta):
 
 * ``linear_layer`` - one linear layer, X ~ N(0,1) [M,K] with a few fixed
   channels multiplied by per-channel factors, W ~ N(0, std) [N,K].
@@ -22,6 +23,8 @@ Workload recipes (stream ids: 1 = X, 2 = W, 3 = outlier channels,
   W fp16 [4096, 4096] ~ N(0, 0.02).
 * ``single_1024``  - X fp32 [16, 1024] ~ N(0,1), channel 0 x50,
   W fp32 [1024, 1024] ~ N(0, 0.03).
+* ``norm_params``  - the parameters of the norm before a layer: gamma fp32
+  [K] ~ N(1, 0.1), beta fp32 [K] ~ N(0, 0.05).
 """
 from __future__ import annotations
 
@@ -181,3 +184,8 @@ def llm_int8_2048(M=2048, N=4096, K=4096, seed=5, n_dims=6):
 def stream_act(M=65536, K=7168, seed=6):
     X, _, ch = linear_layer(seed, M, 1, K, 6, 20.0, 100.0, 0.025)
     return {"X": X, "channels": ch}
+
+
+def norm_params(K, seed=7):
+    """(gamma, beta) fp32 [K] of the norm that feeds a layer."""
+    return normal(seed, 20, (K,), std=0.1, mean=1.0), normal(seed, 21, (K,), std=0.05)

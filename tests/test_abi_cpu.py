@@ -18,11 +18,11 @@ FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced on these p
 def test_exports_every_declared_symbol():
     L = sq.lib()
     declared = sq.header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(L, name), name
         assert name in sq.SIGNATURES, name
-    assert L.sq_version() == 100
+    assert L.sq_version() == 101
 
 
 def test_status_strings():
@@ -115,3 +115,31 @@ def test_binding_requires_gpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         sq.absmax_reduce(torch.zeros(4, 16))
+
+
+def test_fold_norm_validation():
+    L = sq.lib()
+    assert L.sq_fold_norm(FAKE, None, FAKE, -1, FAKE, None, None) == SHAPE
+    assert L.sq_fold_norm(FAKE, None, FAKE, 0, None, None, None) == OK  # nothing to do
+    assert L.sq_fold_norm(None, None, FAKE, 8, FAKE, None, None) == NULL
+    assert L.sq_fold_norm(FAKE, FAKE, FAKE, 8, FAKE, None, None) == NULL  # beta without beta_out
+    assert L.sq_fold_norm(FAKE + 2, None, FAKE, 8, FAKE, None, None) == ALIGN
+
+
+def test_norm_quantize_validation():
+    L = sq.lib()
+    f = L.sq_norm_quantize_act
+    # args: x, dt, M, K, norm, gamma, beta, eps, mode, static_scale, xq, x_scale, stream
+    assert f(FAKE, sq.SQ_F32, 4, 64, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == DTYPE
+    assert f(FAKE, sq.SQ_BF16, 4, 64, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == DTYPE
+    assert f(FAKE, sq.SQ_F16, 4, 64, 2, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == ARG
+    assert f(FAKE, sq.SQ_F16, 4, 64, 0, FAKE, None, -1.0, 1, None, FAKE, FAKE, None) == ARG
+    assert f(FAKE, sq.SQ_F16, 4, 64, 0, FAKE, None, float("inf"), 1, None, FAKE, FAKE, None) == ARG
+    assert f(FAKE, sq.SQ_F16, 4, 64, 0, FAKE, None, 1e-5, 3, None, FAKE, FAKE, None) == ARG
+    assert f(FAKE, sq.SQ_F16, 4, 40, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, sq.SQ_F16, 4, 0, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, sq.SQ_F16, 4, 16400, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, sq.SQ_F16, 4, 64, 0, None, None, 1e-5, 1, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, sq.SQ_F16, 4, 64, 0, FAKE, None, 1e-5, 0, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, sq.SQ_F16, 4, 64, 1, FAKE, FAKE + 4, 1e-5, 1, None, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, sq.SQ_F16, 0, 64, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == OK

@@ -107,7 +107,7 @@ def test_smooth_weights_parity(torch, N, K, dt, smooth):
     (1, 16, "f16", 1, True), (7, 1024, "f32", 0, True), (16, 1024, "f32", 1, False),
     (255, 7168, "f16", 1, True), (257, 7168, "f16", 0, True), (33, 3072, "bf16", 1, True),
     (64, 8208, "f16", 1, True), (3, 16384, "f32", 1, True), (0, 64, "f16", 0, True),
-    (40, 4096, "bf16", 0, False)])
+    (0, 64, "f16", 1, True), (40, 4096, "bf16", 0, False)])
 def test_quantize_act_parity(torch, M, K, dt, mode, smooth):
     import synth
 

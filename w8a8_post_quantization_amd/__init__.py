@@ -14,6 +14,8 @@ Names follow the C ABI:
   quantize_act       a4  fused X / s -> int8 (per-token or per-tensor)
   gemm_i8_dequant    a5  int8 GEMM with the outer-product dequant epilogue
   int8_mixed_matmul  a6  LLM.int8() mixed decomposition
+  fold_norm          1/s folded into the preceding norm's gamma / beta
+  norm_quantize_act  fused fp16 norm -> int8 (per-token or per-tensor)
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sq.h")
 
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_PER_TENSOR_STATIC, SQ_PER_TOKEN_DYNAMIC = 0, 1
+SQ_NORM_LAYER, SQ_NORM_RMS = 0, 1
 
 _lib = None
 
@@ -46,6 +49,8 @@ SIGNATURES = {
     "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64]),
     "sq_int8_mixed_matmul": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, ctypes.c_size_t,
                                   _P, _I, _P, _P]),
+    "sq_fold_norm": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
+    "sq_norm_quantize_act": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
 }
 
 
@@ -233,3 +238,41 @@ def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, work
           w_f16.data_ptr(), N, float(threshold), workspace.data_ptr(), workspace.numel(),
           y.data_ptr(), _dt(y), _ptr(cnt), _stream(stream))
     return (y, cnt) if with_count else y
+
+
+def fold_norm(gamma, s, beta=None, stream=None):
+    """(gamma / s, beta / s or None): the smoothing folded into the norm."""
+    torch = _torch()
+    _check(gamma, "gamma", (torch.float32,), 1)
+    _check(s, "s", (torch.float32,), 1)
+    if beta is not None:
+        _check(beta, "beta", (torch.float32,), 1)
+    g_out = torch.empty_like(gamma)
+    b_out = None if beta is None else torch.empty_like(beta)
+    _call("sq_fold_norm", gamma.data_ptr(), _ptr(beta), s.data_ptr(), gamma.numel(),
+          g_out.data_ptr(), _ptr(b_out), _stream(stream))
+    return g_out, b_out
+
+
+def norm_quantize_act(x, gamma, beta=None, norm=SQ_NORM_LAYER, eps=1e-5,
+                      mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, out=None, stream=None):
+    """Fused fp16 norm -> int8: (xq int8 [M,K], x_scale fp32 [M] or [1])."""
+    torch = _torch()
+    x2 = x.reshape(-1, x.shape[-1])
+    _check(x2, "x", (torch.float16,))
+    _check(gamma, "gamma", (torch.float32,), 1)
+    if beta is not None:
+        _check(beta, "beta", (torch.float32,), 1)
+    if static_scale is not None:
+        _check(static_scale, "static_scale", (torch.float32,), 1)
+    M, K = x2.shape
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M if mode == SQ_PER_TOKEN_DYNAMIC else 1, dtype=torch.float32,
+                         device=x.device)
+    else:
+        xq, xs = out
+    _call("sq_norm_quantize_act", x2.data_ptr(), _dt(x2), M, K, int(norm), gamma.data_ptr(),
+          _ptr(beta), float(eps), int(mode), _ptr(static_scale), xq.data_ptr(), xs.data_ptr(),
+          _stream(stream))
+    return xq, xs

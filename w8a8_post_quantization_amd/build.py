@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["reduce.hip", "quant.hip", "gemm.hip", "sq_api.cpp"]
+SOURCES = ["reduce.hip", "quant.hip", "gemm.hip", "norm.hip", "sq_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall"]

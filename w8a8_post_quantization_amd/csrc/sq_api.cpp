@@ -60,7 +60,7 @@ const char *sq_status_str(int status) {
     }
 }
 
-int sq_version(void) { return 100; }
+int sq_version(void) { return 101; }
 
 int sq_absmax_reduce(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
                      float *amax_out, void *stream) {
@@ -104,8 +104,8 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *in
     if (!valid_dt(dt)) return SQ_ERR_DTYPE;
     if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;  // no rows, no steps
     if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
-    if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;
     if (M > 0 && K > 0 && (!x || !xq)) return SQ_ERR_NULL;
     if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(inv_s, 16) || !aligned(x_scale, 4) ||
         !aligned(static_scale, 4))
@@ -129,6 +129,44 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
         return SQ_ERR_ALIGN;
     sq::launch_gemm(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
                     acc_out, nullptr, st(stream));
+    return finish();
+}
+
+int sq_fold_norm(const float *gamma, const float *beta, const float *s, int64_t K,
+                 float *gamma_out, float *beta_out, void *stream) {
+    if (K < 0 || K > kMaxDim) return SQ_ERR_SHAPE;
+    if (K == 0) return SQ_OK;
+    if (!gamma || !s || !gamma_out || (beta && !beta_out)) return SQ_ERR_NULL;
+    if (!aligned(gamma, 4) || !aligned(beta, 4) || !aligned(s, 4) || !aligned(gamma_out, 4) ||
+        !aligned(beta_out, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_fold_norm(gamma, beta, s, K, gamma_out, beta ? beta_out : nullptr, st(stream));
+    return finish();
+}
+
+int sq_norm_quantize_act(const void *x, int dt, int64_t M, int64_t K, int norm,
+                         const float *gamma, const float *beta, float eps, int mode,
+                         const float *static_scale, int8_t *xq, float *x_scale, void *stream) {
+    if (dt != SQ_F16) return SQ_ERR_DTYPE;
+    if (norm != SQ_NORM_LAYER && norm != SQ_NORM_RMS) return SQ_ERR_ARG;
+    if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return SQ_ERR_ARG;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (M > 0 && K == 0) return SQ_ERR_SHAPE;  // the mean of an empty row is undefined
+    if (K > 16384) return SQ_ERR_UNSUPPORTED;
+    if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;  // no rows, no steps
+    if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
+    if (M == 0) {  // the per-tensor step is still reported
+        if (!aligned(x_scale, 4) || !aligned(static_scale, 4)) return SQ_ERR_ALIGN;
+        sq::launch_copy_f32(static_scale, x_scale, st(stream));
+        return finish();
+    }
+    if (!x || !xq || !gamma) return SQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 16) || !aligned(beta, 16) ||
+        !aligned(x_scale, 4) || !aligned(static_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_norm_quant(x, M, K, norm, gamma, beta, eps, mode == SQ_PER_TOKEN_DYNAMIC,
+                          static_scale, xq, x_scale, st(stream));
     return finish();
 }
 

@@ -37,6 +37,14 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
 void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
                          float *mask, int32_t *idx, int32_t *count, hipStream_t stream);
 
+// Folding 1/s into the norm's parameters, and the fused fp16 norm ->
+// int8 row quantizer (K <= 16384).
+void launch_fold_norm(const float *gamma, const float *beta, const float *s, int64_t K,
+                      float *gamma_out, float *beta_out, hipStream_t stream);
+void launch_norm_quant(const void *x, int64_t M, int64_t K, int norm, const float *gamma,
+                       const float *beta, float eps, int dynamic, const float *static_scale,
+                       int8_t *q, float *scale, hipStream_t stream);
+
 // Tiny device-to-device copies done by a kernel (no copy-engine or memset
 // nodes, so the calls stay capturable in a HIP graph).
 void launch_copy_i32(const int32_t *src, int32_t *dst, hipStream_t stream);
