@@ -54,9 +54,10 @@ def test_fold_norm_parity(torch):
     (256, 7168, 0, True, 1), (256, 7168, 1, False, 1), (5, 16384, 0, False, 1),
     (64, 4096, 1, True, 0), (40, 2064, 0, True, 0), (2, 8208, 0, True, 1), (0, 64, 0, True, 0),
     (0, 64, 1, False, 1), (300, 512, 0, False, 1),
-    # many rows: the wave-per-row kernel (gamma / beta staged in LDS)
+    # many rows: blocks walk several rows (beta staged in LDS up to K = 8192)
     (2048, 1024, 0, True, 1), (2100, 4096, 1, False, 1), (2051, 48, 1, True, 1),
-    (4096, 8192, 0, True, 0), (2304, 7168, 0, True, 1), (2049, 2064, 1, True, 0)])
+    (4096, 8192, 0, True, 0), (2304, 7168, 0, True, 1), (2049, 2064, 1, True, 0),
+    (2050, 8208, 0, True, 1)])
 def test_norm_quantize_parity(torch, M, K, norm, with_beta, mode):
     x = _x(M * 31 + K, M, K)
     g, b = synth.norm_params(K, seed=M + K)

@@ -8,7 +8,8 @@
 // Row statistics are exact.  An fp16 value times 2^24 is an integer below
 // 2^40 (subnormals included), so S1 = sum x 2^24 fits int64 and
 // S2 = sum (x 2^24)^2 fits 128 bits, and both are independent of the order
-// in which the block adds them up (K <= 16384).  From them, in double:
+// in which the block adds them up (K <= 16384).  The kernel forms them from
+// sums in double that never round (see norm_quant_kernel).  From them:
 //   layer norm: mu = S1 / (K 2^24), sigma^2 = (K S2 - S1^2) / (K^2 2^48)
 //   RMS norm:   mu = 0,             sigma^2 = S2 / (K 2^48)
 //   rstd = 1 / sqrt(sigma^2 + eps)
@@ -36,12 +37,6 @@ __global__ void fold_norm_kernel(const float *__restrict__ gamma, const float *_
     if (beta) beta_out[j] = b / sj;
 }
 
-// fp16 bits -> |x| 2^24 (exact integer) and its sign.
-__device__ __forceinline__ uint64_t f16_fixed_mag(uint32_t h) {
-    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
-    return e ? (uint64_t)(1024u | m) << (e - 1) : (uint64_t)m;
-}
-
 __device__ __forceinline__ double u128_to_double(u128 v) {
     const uint64_t hi = (uint64_t)(v >> 64), lo = (uint64_t)v;
     return (double)hi * 18446744073709551616.0 + (double)lo;
@@ -65,15 +60,53 @@ __device__ __forceinline__ void norm_stats(int64_t S1, u128 S2, int64_t K, float
     rstd = (float)(1.0 / sqrt(var + (double)eps));
 }
 
+// Wave sums and maxima through DPP lane moves (no LDS round trip): four
+// steps leave each 16-lane row's total in all its lanes, two row broadcasts
+// then carry the wave's total into lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i32(int v) {
+    if constexpr (ROWS == 0xf) return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+    else return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);  // other rows: 0
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)dpp_i32<CTRL, ROWS>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)dpp_i32<CTRL, ROWS>((int)(uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror,
+// row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3.
+__device__ __forceinline__ double wave_sum_to_last(double v) {
+    v += dpp_f64<0xb1, 0xf>(v);
+    v += dpp_f64<0x4e, 0xf>(v);
+    v += dpp_f64<0x141, 0xf>(v);
+    v += dpp_f64<0x140, 0xf>(v);
+    v += dpp_f64<0x142, 0xa>(v);
+    v += dpp_f64<0x143, 0xc>(v);
+    return v;
+}
+// Non-negative inputs: lanes outside a broadcast's rows read 0.
+__device__ __forceinline__ float wave_max_to_last(float v) {
+    v = fmaxf(v, __int_as_float(dpp_i32<0xb1, 0xf>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x4e, 0xf>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x141, 0xf>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x140, 0xf>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x142, 0xa>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x143, 0xc>(__float_as_int(v))));
+    return v;
+}
+
 // A 256-thread block per row, walking rows_per_block consecutive rows; ITS
 // 16-byte vectors (8 fp16) per thread.  Every load is unconditional, with
 // out-of-range vector indices clamped to the row's last vector (loaded, not
 // used): a load under a lane-divergent branch would wait for all earlier
 // memory operations.  The row's sums and maximum are combined across the 4
 // waves through LDS slots that alternate between consecutive rows, so one
-// barrier per reduction suffices.  The ALU work of the exact sums (a 128-bit
-// multiply-add per element), not HBM, bounds the kernel on long streams.
-template <int ITS, int NORM, bool HAS_BETA, bool DYN>
+// barrier per exchange suffices.  (Four waves per row, one per SIMD, keep
+// the work between barriers even across the SIMDs; more waves per row
+// repeat the per-row reductions more often.)
+template <int ITS, int NORM, bool HAS_BETA, bool DYN, bool BETA_LDS>
 __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
                                                          const float *__restrict__ gamma,
@@ -83,34 +116,45 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
                                                          int8_t *__restrict__ q,
                                                          float *__restrict__ scale,
                                                          int rows_per_block) {
+    constexpr int T = 256;
     __shared__ int64_t sh_s1[2][4];
-    __shared__ uint64_t sh_lo[2][4], sh_hi[2][4];
+    __shared__ int64_t sh_lo[2][4], sh_hi[2][4];
     __shared__ float sh_max[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // wave-uniform
     if (!DYN && blockIdx.x == 0 && tid == 0) scale[0] = static_scale[0];
     const int64_t nvec = K / 8;
 
-    // gamma / beta of this thread's vectors: loaded once for all the
-    // block's rows.
-    float4 g[ITS][2], b[HAS_BETA ? ITS : 1][2];
+    // gamma (and, for rows of up to 16 K bytes, beta too) of this thread's
+    // vectors stay in registers, loaded once for all the block's rows.
+    // Otherwise beta is staged in LDS (K floats, dynamic shared memory):
+    // that frees 8 ITS registers, enough for a third wave per SIMD.
+    constexpr bool BETA_REG = HAS_BETA && !BETA_LDS;
+    float4 g[ITS][2], b[BETA_REG ? ITS : 1][2];
 #pragma unroll
     for (int it = 0; it < ITS; ++it) {
-        const int64_t vi = tid + (int64_t)it * 256;
+        const int64_t vi = tid + (int64_t)it * T;
         const int64_t vc = vi < nvec ? vi : nvec - 1;
         const float4 *gp = reinterpret_cast<const float4 *>(gamma + vc * 8);
         g[it][0] = gp[0];
         g[it][1] = gp[1];
-        if constexpr (HAS_BETA) {
+        if constexpr (BETA_REG) {
             const float4 *bp = reinterpret_cast<const float4 *>(beta + vc * 8);
             b[it][0] = bp[0];
             b[it][1] = bp[1];
         }
     }
+    extern __shared__ float4 sh_beta[];  // [K / 4] when BETA_LDS
+    if constexpr (BETA_LDS) {
+        const float4 *bp = reinterpret_cast<const float4 *>(beta);
+        for (int64_t i = tid; i < K / 4; i += T) sh_beta[i] = bp[i];
+        __syncthreads();
+    }
     auto load_row = [&](int64_t r, uint4 (&raw)[ITS]) {
         const uint4 *xr = x + r * nvec;
 #pragma unroll
         for (int it = 0; it < ITS; ++it) {
-            const int64_t vi = tid + (int64_t)it * 256;
+            const int64_t vi = tid + (int64_t)it * T;
             raw[it] = ld_nt(xr + (vi < nvec ? vi : nvec - 1));
         }
     };
@@ -122,89 +166,96 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
     // barrier every wave reaches once it has read the slot.
     auto process = [&](int64_t r, const uint4 (&raw)[ITS], auto par_c) {
         constexpr int PAR = decltype(par_c)::value;
-        // Exact row sums.  sum x in double: every term is a multiple of 2^-24
-        // and |sum| < 16384 * 65504 < 2^30, so no partial sum ever rounds.
-        // sum (x 2^24)^2 = sum M^2 2^(2s) (x 2^24 = M 2^s, M the 11-bit
-        // significand, a term < 2^80) is kept as two carry-free 64-bit sums of
-        // the term's bits above and below bit 32: hi parts < 2^48 and lo parts
-        // < 2^32 add up over a whole row (16384 terms) without overflow, and the
-        // sum is hi 2^32 + lo.
-        double s1d = 0.0;
-        uint64_t hi = 0, lo = 0;
+        // Exact row sums in double.  sum x: every term is a multiple of 2^-24
+        // and a wave's |sum| < 4096 * 65504 < 2^28, so no partial sum rounds.
+        // sum x^2: x^2 is exact in double; fma(x, x, C) with C = 1.5 2^45
+        // lands in [2^45, 2^46), where the spacing is 2^-7, so
+        // h = fma(x, x, C) - C is x^2 rounded to a multiple of 2^-7 and
+        // l = fma(x, x, -h) = x^2 - h is exact (a multiple of 2^-48, |l| <=
+        // 2^-8).  A wave adds at most 512 ITS <= 4096 terms: the h sum stays
+        // below 2^44 (2^51 steps of 2^-7) and the l sum below 2^4 (2^52 steps
+        // of 2^-48), so neither ever rounds, in any order.  Each wave's three sums are
+        // then exact integers in units of 2^-24, 2^-7 and 2^-48.
+        constexpr double kSplit = 52776558133248.0;  // 1.5 * 2^45
+        double s1d = 0.0, shi = 0.0, slo = 0.0;
     #pragma unroll
         for (int it = 0; it < ITS; ++it) {
-            if (tid + (int64_t)it * 256 < nvec) {
-                const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+            if (tid + (int64_t)it * T < nvec) {
                 float v[8];
                 widen16<F16>(raw[it], v);
     #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    s1d += (double)v[e];
-                    const uint32_t ex = (h >> 10) & 31u;
-                    const uint32_t m = (h & 1023u) | (ex ? 1024u : 0u);
-                    const uint32_t sh = ex ? 2u * (ex - 1u) : 0u;      // 0 .. 58
-                    const uint32_t sl = sh < 32u ? sh : 32u;
-                    const uint64_t full = (uint64_t)(m * m) << sl;      // m^2 < 2^22
-                    lo += (uint32_t)full;                               // bits 0 .. 31
-                    hi += (full >> 32) << (sh - sl);                    // bits 32 .. 79, / 2^32
+                    const double d = (double)v[e];
+                    if constexpr (NORM == 0) s1d += d;
+                    const double h = __builtin_fma(d, d, kSplit) - kSplit;
+                    shi += h;
+                    slo += __builtin_fma(d, d, -h);
                 }
             }
         }
-    #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            s1d += __shfl_xor(s1d, off, kWave);
-            hi += __shfl_xor(hi, off, kWave);
-            lo += __shfl_xor(lo, off, kWave);
-        }
-        const int64_t s1 = (int64_t)(s1d * 16777216.0);  // exact: an integer below 2^54
-        if (lane == 0) {
-            sh_s1[PAR][wave] = s1;
-            sh_lo[PAR][wave] = lo;
-            sh_hi[PAR][wave] = hi;
+        if constexpr (NORM == 0) s1d = wave_sum_to_last(s1d);
+        shi = wave_sum_to_last(shi);
+        slo = wave_sum_to_last(slo);
+        if (lane == 63) {
+            sh_s1[PAR][wave] = (int64_t)(s1d * 16777216.0);        // x 2^24
+            sh_hi[PAR][wave] = (int64_t)(shi * 128.0);             // x^2 2^7
+            sh_lo[PAR][wave] = (int64_t)(slo * 281474976710656.0); // x^2 2^48
         }
         __syncthreads();
-        int64_t S1 = 0;
-        uint64_t H = 0, Lo = 0;
+        // Row totals: |S1| < 2^54, H < 2^53, |L| < 2^54; the row's
+        // sum (x 2^24)^2 = H 2^41 + L.
+        int64_t S1 = 0, H = 0, L = 0;
     #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            S1 += sh_s1[PAR][w];
+            if constexpr (NORM == 0) S1 += sh_s1[PAR][w];
             H += sh_hi[PAR][w];
-            Lo += sh_lo[PAR][w];
+            L += sh_lo[PAR][w];
         }
-        const u128 S2 = ((u128)H << 32) + Lo;
-
+        const u128 S2 = (u128)(((__int128)H << 41) + L);
         float mu, rstd;
         norm_stats<NORM>(S1, S2, K, eps, mu, rstd);
 
         // The normalized, scaled row (kept in registers for the store pass).
+        // Slots past the row's end hold copies of its last vector (clamped
+        // loads of x, gamma and beta), so they may enter the maximum; slots
+        // no lane of this wave owns are skipped on a scalar branch.
         float y[ITS][8];
         float amax = 0.0f;
     #pragma unroll
         for (int it = 0; it < ITS; ++it) {
+            if (wave_base + it * T >= nvec) continue;
             float v[8];
             widen16<F16>(raw[it], v);
             const float gv[8] = {g[it][0].x, g[it][0].y, g[it][0].z, g[it][0].w,
                                  g[it][1].x, g[it][1].y, g[it][1].z, g[it][1].w};
-            const bool live = tid + (int64_t)it * 256 < nvec;
+            float4 bl[2];
+            if constexpr (BETA_LDS) {
+                const int64_t vi = tid + (int64_t)it * T;
+                const int64_t vc = vi < nvec ? vi : nvec - 1;
+                bl[0] = sh_beta[vc * 2];
+                bl[1] = sh_beta[vc * 2 + 1];
+            } else if constexpr (BETA_REG) {
+                bl[0] = b[it][0];
+                bl[1] = b[it][1];
+            }
     #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float n = NORM == 0 ? (v[e] - mu) * rstd : v[e] * rstd;
                 float t = n * gv[e];
                 if constexpr (HAS_BETA) {
-                    const float bv[8] = {b[it][0].x, b[it][0].y, b[it][0].z, b[it][0].w,
-                                         b[it][1].x, b[it][1].y, b[it][1].z, b[it][1].w};
+                    const float bv[8] = {bl[0].x, bl[0].y, bl[0].z, bl[0].w,
+                                         bl[1].x, bl[1].y, bl[1].z, bl[1].w};
                     t = t + bv[e];
                 }
                 y[it][e] = t;
-                if (live) amax = fmaxf(amax, fabsf(t));
+                amax = fmaxf(amax, fabsf(t));
             }
         }
 
         float inv;
         if constexpr (DYN) {
-            amax = wave_max(amax);
-            if (lane == 0) sh_max[PAR][wave] = amax;
+            amax = wave_max_to_last(amax);
+            if (lane == 63) sh_max[PAR][wave] = amax;
             __syncthreads();
             float a = fmaxf(fmaxf(sh_max[PAR][0], sh_max[PAR][1]), fmaxf(sh_max[PAR][2], sh_max[PAR][3]));
             if (!(a > 1e-8f)) a = 1e-8f;
@@ -213,16 +264,34 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
         } else {
             inv = static_scale[1];
         }
+        // q = clamp(rint(fl(y inv)), -127, 127).  Adding 1.5 2^23 to a value
+        // of magnitude below 2^22 rounds it to an integer, half to even, and
+        // leaves that integer's two's complement low byte in the low byte of
+        // the sum's bits.  With the per-token step |y| <= a, so
+        // |fl(y inv)| <= 127 (1 + 2^-24) and the clamp never acts; with a
+        // fixed step the product is clamped first (rint and the clamp commute
+        // at integer bounds).
         int8_t *qr = q + r * K;
     #pragma unroll
         for (int it = 0; it < ITS; ++it) {
-            const int64_t vi = tid + (int64_t)it * 256;
+            if (wave_base + it * T >= nvec) continue;
+            uint32_t bits[8];
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float z = y[it][e] * inv;
+                if constexpr (!DYN) z = __builtin_amdgcn_fmed3f(z, -127.0f, 127.0f);
+                bits[e] = __float_as_uint(z + 12582912.0f);
+            }
+            const int64_t vi = tid + (int64_t)it * T;
             if (vi < nvec) {
+                // low bytes of bits[0..3] -> one word: [b0 b1 0 0] | [b2 b3 0 0] << 16
                 uint2 o;
-                o.x = pack4(quant_i8(y[it][0], inv), quant_i8(y[it][1], inv), quant_i8(y[it][2], inv),
-                            quant_i8(y[it][3], inv));
-                o.y = pack4(quant_i8(y[it][4], inv), quant_i8(y[it][5], inv), quant_i8(y[it][6], inv),
-                            quant_i8(y[it][7], inv));
+                o.x = __builtin_amdgcn_perm(__builtin_amdgcn_perm(bits[3], bits[2], 0x0c0c0400u),
+                                            __builtin_amdgcn_perm(bits[1], bits[0], 0x0c0c0400u),
+                                            0x05040100u);
+                o.y = __builtin_amdgcn_perm(__builtin_amdgcn_perm(bits[7], bits[6], 0x0c0c0400u),
+                                            __builtin_amdgcn_perm(bits[5], bits[4], 0x0c0c0400u),
+                                            0x05040100u);
                 *reinterpret_cast<uint2 *>(qr + vi * 8) = o;
             }
         }
@@ -262,16 +331,24 @@ static void launch_nq(const void *x, int64_t M, int64_t K, const float *gamma,
     if (rpb < 1) rpb = 1;
     dim3 grid((unsigned)((M + rpb - 1) / rpb)), block(256);
     auto *xv = reinterpret_cast<const uint4 *>(x);
-#define SQ_NQ(HB, DY)                                                                          \
-    norm_quant_kernel<ITS, NORM, HB, DY><<<grid, block, 0, stream>>>(xv, M, K, gamma, beta,     \
-                                                                   eps, static_scale, q, scale, \
-                                                                   (int)rpb)
-    if (beta) {
-        if (dynamic) SQ_NQ(true, true);
-        else SQ_NQ(true, false);
+    // Beta goes to LDS when the block walks several rows (the staging
+    // costs more than it saves for one row) and the row fits (ITS <= 4).
+    const bool beta_lds = beta && ITS <= 4 && rpb > 1;
+    const size_t lds = beta_lds ? (size_t)K * sizeof(float) : 0;
+#define SQ_NQ(HB, DY, BL)                                                                      \
+    norm_quant_kernel<ITS, NORM, HB, DY, BL><<<grid, block, lds, stream>>>(                     \
+        xv, M, K, gamma, beta, eps, static_scale, q, scale, (int)rpb)
+    if (beta_lds) {
+        if constexpr (ITS <= 4) {
+            if (dynamic) SQ_NQ(true, true, true);
+            else SQ_NQ(true, false, true);
+        }
+    } else if (beta) {
+        if (dynamic) SQ_NQ(true, true, false);
+        else SQ_NQ(true, false, false);
     } else {
-        if (dynamic) SQ_NQ(false, true);
-        else SQ_NQ(false, false);
+        if (dynamic) SQ_NQ(false, true, false);
+        else SQ_NQ(false, false, false);
     }
 #undef SQ_NQ
 }
