@@ -63,6 +63,7 @@ def lib():
             "orc_smooth_weights_f32": (None, [_P, _I, _I64, _I64, _P, _P]),
             "orc_quantize_rows_f32": (None, [_P, _I64, _I64, _P, _P]),
             "orc_smooth_weights": (None, [_P, _I, _I64, _I64, _P, _P, _P]),
+            "orc_fold_smooth_weights": (None, [_P, _I, _I64, _I64, _P, _P, _P, _P]),
             "orc_quantize_act": (None, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P]),
             "orc_gemm_i8_dequant": (_I64, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P]),
             "orc_gemm_i8_dequant_at": (None, [_P, _P, _I64, _P, _I, _P, _I, _P, _P, _I64, _P, _P]),
@@ -157,6 +158,21 @@ def smooth_weights(w, s=None):
     if s is not None:
         s = _c(s.astype(np.float32, copy=False))
     lib().orc_smooth_weights(w.ctypes.data, _dt(w), N, K, _ptr(s), wq.ctypes.data, ws.ctypes.data)
+    return wq, ws
+
+
+def fold_smooth_weights(w, row_mul=None, s=None):
+    """a3 with the next layer's 1/s folded into the output rows (row_mul)."""
+    w = _c(w)
+    N, K = w.shape
+    wq = np.empty((N, K), np.int8)
+    ws = np.empty(N, np.float32)
+    if s is not None:
+        s = _c(s.astype(np.float32, copy=False))
+    if row_mul is not None:
+        row_mul = _c(row_mul.astype(np.float32, copy=False))
+    lib().orc_fold_smooth_weights(w.ctypes.data, _dt(w), N, K, _ptr(row_mul), _ptr(s),
+                                  wq.ctypes.data, ws.ctypes.data)
     return wq, ws
 
 

@@ -212,6 +212,25 @@ void orc_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
     }
 }
 
+void orc_fold_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
+                             const float *row_mul, const float *s, int8_t *wq,
+                             float *w_scale) {
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) {
+                float v = load_elem(w, dt, n * K + k);
+                if (row_mul) v = v * row_mul[n];
+                row[k] = s ? v * s[k] : v;
+            }
+            quantize_row(row, K, wq + n * K, &w_scale[n]);
+        }
+        free(row);
+    }
+}
+
 /* ------------------------------------------------- a4: activations */
 
 void orc_quantize_act(const void *x, int dt, int64_t M, int64_t K,

@@ -95,6 +95,20 @@ void orc_quantize_rows_f32(const float *v, int64_t rows, int64_t K, int8_t *q,
 void orc_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
                         const float *s, int8_t *wq, float *w_scale);
 
+/* a3 with the next layer's smoothing folded into this layer's output
+ * channels: W''[n, k] = fl(fl(W[n, k] * row_mul[n]) * s[k]) (row_mul == NULL:
+ * no row factor; s == NULL: no column factor), then the row quantizer above.
+ * [SQ-tutorial] 融入前序线性层的权重: down_proj's input channel j is shrunk by
+ * 1/s_j by multiplying up_proj's output channel j by 1/s_j (likewise v_proj
+ * for o_proj), so row_mul is the next layer's inv_s; this layer's own input
+ * smoothing s still scales its columns.  The row factor is applied first
+ * (the fold rewrites the stored weight, the smoothing then acts on it).
+ * Pinned: row_mul = 1 gives a3; power-of-two row_mul gives a3's codes with
+ * the steps scaled exactly; dequantized W'' against diag(r) W diag(s). */
+void orc_fold_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
+                             const float *row_mul, const float *s, int8_t *wq,
+                             float *w_scale);
+
 /* a4: xs = fl(X * inv_s) (inv_s == NULL: xs = X), then
  *   mode PER_TOKEN_DYNAMIC: the row quantizer above, x_scale[M];
  *   mode PER_TENSOR_STATIC: q = clamp(rhe(fl(xs * static_scale[1]))),
