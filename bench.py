@@ -407,6 +407,27 @@ def extras(torch, L, _sp, T, chk):
     res["decoder_1024"] = {"per_gemm": per, "total_us": round(total_us, 2),
                            "TOPS": round(total_ops / total_us / 1e6, 1),
                            "frac_int8_peak": round(total_ops / total_us / 1e6 / PEAK_INT8_TOPS, 4)}
+    # The same layer with shared-input groups batched: q|k|v share one s and
+    # become one GEMM (N = 4096), gate|up another (N = 6144).
+    dims = {n: (nn, kk) for n, nn, kk in synth.DECODER_1024_WEIGHTS}
+    groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+              ("down", ("down",))]
+    total_us, total_ops, per = 0.0, 0.0, {}
+    for gname, members in groups:
+        n = sum(dims[m][0] for m in members)
+        k = dims[members[0]][1]
+        xq, wq, xs, ws = R(M, k), R(n, k), U(M, 1e-2), U(n, 1e-3)
+        y = torch.empty((M, n), dtype=torch.float16, device=dev)
+        us = _time_loop(torch, [lambda: chk(L.sq_gemm_i8_dequant(
+            P(xq), P(wq), M, n, k, P(xs), 1, P(ws), P(y), 1, None, sp), "dec1024b")], 50)
+        ops = 2.0 * M * n * k
+        per[gname] = {"N": n, "K": k, "us": round(us, 2), "TOPS": round(ops / us / 1e6, 1)}
+        total_us += us
+        total_ops += ops
+    res["decoder_1024_batched"] = {
+        "per_gemm": per, "total_us": round(total_us, 2),
+        "TOPS": round(total_ops / total_us / 1e6, 1),
+        "frac_int8_peak": round(total_ops / total_us / 1e6 / PEAK_INT8_TOPS, 4)}
     return res
 
 

@@ -133,6 +133,24 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
                     int8_t *xq, float *x_scale, void *stream);
 
 /*
+ * a3 with the next layer's smoothing folded into this layer's output
+ * channels.  [SQ-tutorial] 融入前序线性层的权重 and its table of fold
+ * positions: down_proj's input channel j must shrink by 1/s_j, which is done
+ * by multiplying up_proj's output channel j by 1/s_j (o_proj's smoothing
+ * likewise goes into v_proj); this layer's own input smoothing s still
+ * scales its columns.
+ *   w        [N, K] of dt (e.g. up_proj or v_proj)
+ *   row_mul  [N] fp32 (the next layer's inv_s), or NULL (= sq_smooth_weights)
+ *   s        [K] fp32, or NULL (this layer's columns unscaled)
+ *   wq, w_scale as sq_smooth_weights, of w''[n, k] = fl(fl(w * row_mul[n]) * s[k]).
+ * The next layer then quantizes its input with inv_s = NULL (the division
+ * already happened here).  K % 16 == 0; row_mul 4-byte aligned.
+ */
+int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K,
+                             const float *row_mul, const float *s, int8_t *wq,
+                             float *w_scale, void *stream);
+
+/*
  * a5 - int8 x int8 -> int32 GEMM with the outer-product dequant epilogue.
  * [SQ-tutorial] Y = diag(delta_X) X_int8 W_int8 diag(delta_W);
  * [INT8-expl] §2.1 (int32 accumulation, c_x (x) c_w).

@@ -18,11 +18,11 @@ FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced on these p
 def test_exports_every_declared_symbol():
     L = sq.lib()
     declared = sq.header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     for name in declared:
         assert hasattr(L, name), name
         assert name in sq.SIGNATURES, name
-    assert L.sq_version() == 101
+    assert L.sq_version() == 102
 
 
 def test_status_strings():
@@ -61,6 +61,13 @@ def test_smooth_and_quantize_validation():
     assert L.sq_smooth_weights(None, sq.SQ_F16, 8, 32, None, FAKE, FAKE, None) == NULL
     assert L.sq_smooth_weights(FAKE, sq.SQ_F16, 8, 32, FAKE + 4, FAKE, FAKE, None) == ALIGN
     assert L.sq_smooth_weights(None, sq.SQ_F16, 0, 32, None, None, None, None) == OK
+    f = L.sq_smooth_weights_folded
+    assert f(FAKE, sq.SQ_F16, 8, 24, FAKE, None, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 5, 8, 32, FAKE, None, FAKE, FAKE, None) == DTYPE
+    assert f(FAKE, sq.SQ_F16, 8, 32, FAKE, None, None, FAKE, None) == NULL
+    assert f(FAKE, sq.SQ_F16, 8, 32, FAKE + 2, None, FAKE, FAKE, None) == ALIGN   # row_mul
+    assert f(FAKE, sq.SQ_F16, 8, 32, FAKE, FAKE + 4, FAKE, FAKE, None) == ALIGN   # s
+    assert f(None, sq.SQ_F16, 0, 32, None, None, None, None, None) == OK
     assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 32, None, 3, None, FAKE, FAKE, None) == ARG
     assert L.sq_quantize_act(FAKE, sq.SQ_F16, 8, 32, None, sq.SQ_PER_TENSOR_STATIC, None,
                              FAKE, FAKE, None) == NULL

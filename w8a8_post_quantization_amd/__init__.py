@@ -44,6 +44,7 @@ SIGNATURES = {
     "sq_absmax_reduce": (_I, [_P, _I, _I64, _I64, _I, _P, _P]),
     "sq_compute_scales": (_I, [_P, _P, _I64, _F, _P, _P, _P, _P]),
     "sq_smooth_weights": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P]),
+    "sq_smooth_weights_folded": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P]),
     "sq_quantize_act": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "sq_gemm_i8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P, _P]),
     "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64]),
@@ -154,17 +155,28 @@ def compute_scales(act_amax, w_amax, alpha, static=False, stream=None):
     return (s, inv, st) if static else (s, inv)
 
 
-def smooth_weights(w, s=None, stream=None):
-    """a3: (wq int8 [N,K], w_scale fp32 [N])."""
+def smooth_weights(w, s=None, row_mul=None, stream=None):
+    """a3: (wq int8 [N,K], w_scale fp32 [N]).  row_mul [N]: the next layer's
+    inv_s folded into this layer's output channels (sq_smooth_weights_folded)."""
     torch = _torch()
     _check(w, "w", (torch.float32, torch.float16, torch.bfloat16), 2)
     if s is not None:
         _check(s, "s", (torch.float32,), 1)
     N, K = w.shape
+    if row_mul is not None:
+        _check(row_mul, "row_mul", (torch.float32,), 1)
+        if row_mul.numel() != N:
+            raise ValueError(f"row_mul has {row_mul.numel()} elements, w has {N} rows")
+    if s is not None and s.numel() != K:
+        raise ValueError(f"s has {s.numel()} elements, w has {K} columns")
     wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     ws = torch.empty(N, dtype=torch.float32, device=w.device)
-    _call("sq_smooth_weights", w.data_ptr(), _dt(w), N, K, _ptr(s), wq.data_ptr(),
-          ws.data_ptr(), _stream(stream))
+    if row_mul is None:
+        _call("sq_smooth_weights", w.data_ptr(), _dt(w), N, K, _ptr(s), wq.data_ptr(),
+              ws.data_ptr(), _stream(stream))
+    else:
+        _call("sq_smooth_weights_folded", w.data_ptr(), _dt(w), N, K, _ptr(row_mul), _ptr(s),
+              wq.data_ptr(), ws.data_ptr(), _stream(stream))
     return wq, ws
 
 

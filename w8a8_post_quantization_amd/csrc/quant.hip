@@ -13,6 +13,10 @@
 //    0/1 column mask; the xdnf.cn explainer §2.2).  Multiplying by 1.0 is
 //    exact and by 0.0 gives +-0, which quantizes to 0, the same as
 //    removing the column.
+// Weights may also carry a per-row factor applied first,
+// v = fl(fl(x[r, k] * row_mul[r]) * mul[k]): the next layer's 1/s folded
+// into this layer's output channels (the SmoothQuant tutorial page, section
+// 融入前序线性层的权重: up_proj for down_proj, v_proj for o_proj).
 //
 // One 64-lane wave per row (or, for few rows, one 256-thread block per
 // row).  Each lane keeps its 16-byte vectors of the row in registers (up to
@@ -40,11 +44,15 @@ __device__ __forceinline__ void load_mul(const float *__restrict__ mul, int64_t 
 
 extern __shared__ float4 smul4[];
 
-template <int DT, bool HAS_MUL, bool MUL_LDS>
+template <int DT, bool HAS_MUL, bool MUL_LDS, bool HAS_ROW = false>
 __device__ __forceinline__ void scaled(const uint4 &raw, const float *__restrict__ mul,
-                                       int64_t e0, float *v) {
+                                       int64_t e0, float *v, float rm = 1.0f) {
     constexpr int V = Vec<DT>::n;
     widen16<DT>(raw, v);
+    if constexpr (HAS_ROW) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) v[i] = v[i] * rm;
+    }
     if constexpr (HAS_MUL) {
         float m[V];
         if constexpr (MUL_LDS) {
@@ -93,10 +101,11 @@ constexpr int kMulLds = 16384;
 // branch makes the compiler wait for all earlier memory operations first,
 // which would serialize the row's loads.  ITS = 0: rows longer than
 // 16 x 64 vectors, streamed twice (the second pass hits L2).
-template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS>
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
                                                          const float *__restrict__ mul_g,
+                                                         const float *__restrict__ row_mul,
                                                          const float *__restrict__ static_scale,
                                                          int8_t *__restrict__ q,
                                                          float *__restrict__ scale,
@@ -133,13 +142,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             }
         };
         auto finish_row = [&](int64_t r, const uint4 (&b)[ITS]) {
+            const float rm = HAS_ROW ? row_mul[r] : 1.0f;
             float a = 0.0f;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
                 const int64_t vc = vi < nvec ? vi : nvec - 1;
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS>(b[it], mul, vc * V, v);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(b[it], mul, vc * V, v, rm);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 const int64_t vi = lane + (int64_t)it * kWave;
                 if (vi < nvec) {
                     float v[V];
-                    scaled<DT, HAS_MUL, MUL_LDS>(raw, mul, vi * V, v);
+                    scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm);
                     store_q<DT>(qr, vi * V, v, inv);
                 }
             }
@@ -189,10 +199,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
         const uint4 *xr = x + r * nvec;
         int8_t *qr = q + r * K;
         if constexpr (DYN) {
+            const float rm = HAS_ROW ? row_mul[r] : 1.0f;
             float a = 0.0f;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             if (lane == 0) scale[r] = a / 127.0f;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
                 store_q<DT>(qr, vi * V, v, inv);
             }
         } else {
@@ -220,10 +231,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
 // before the reduction; the row maximum is combined across the 4 waves
 // through LDS.  Out-of-range vector indices are clamped to the row's last
 // vector (loaded, not used) so every load is unconditional.
-template <int DT, bool HAS_MUL, bool DYN, int ITS>
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool HAS_ROW>
 __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__restrict__ x,
                                                               int64_t K,
                                                               const float *__restrict__ mul,
+                                                              const float *__restrict__ row_mul,
                                                               const float *__restrict__ static_scale,
                                                               int8_t *__restrict__ q,
                                                               float *__restrict__ scale) {
@@ -243,6 +255,7 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
         raw[it] = ld_nt(xr + vc);
         if constexpr (HAS_MUL) load_mul<DT>(mul, vc * V, m[it]);
     }
+    const float rm = HAS_ROW ? row_mul[r] : 1.0f;
     float inv;
     if constexpr (DYN) {
         float a = 0.0f;
@@ -253,6 +266,7 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
             widen16<DT>(raw[it], v);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                if constexpr (HAS_ROW) v[i] = v[i] * rm;
                 if constexpr (HAS_MUL) v[i] = v[i] * m[it][i];
                 if (vi < nvec) a = fmaxf(a, fabsf(v[i]));
             }
@@ -274,6 +288,10 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
         if (vi < nvec) {
             float v[V];
             widen16<DT>(raw[it], v);
+            if constexpr (HAS_ROW) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) v[i] = v[i] * rm;
+            }
             if constexpr (HAS_MUL) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) v[i] = v[i] * m[it][i];
@@ -283,9 +301,10 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
     }
 }
 
-template <int DT, bool HAS_MUL, bool DYN>
+template <int DT, bool HAS_MUL, bool DYN, bool HAS_ROW = false>
 static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
-                     const float *static_scale, int8_t *q, float *scale, hipStream_t stream) {
+                     const float *static_scale, int8_t *q, float *scale, hipStream_t stream,
+                     const float *row_mul = nullptr) {
     auto *xv = reinterpret_cast<const uint4 *>(x);
     const int64_t nvec = K / Vec<DT>::n;
     // Fewer rows than ~2 waves per SIMD of the chip, and long enough rows:
@@ -294,7 +313,8 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
         const int64_t its = (nvec + 255) / 256;
         dim3 grid((unsigned)rows), block(256);
 #define SQ_B(ITS) \
-    quant_row_block_kernel<DT, HAS_MUL, DYN, ITS><<<grid, block, 0, stream>>>(xv, K, mul, static_scale, q, scale)
+    quant_row_block_kernel<DT, HAS_MUL, DYN, ITS, HAS_ROW><<<grid, block, 0, stream>>>(        \
+        xv, K, mul, row_mul, static_scale, q, scale)
         if (its <= 1) SQ_B(1);
         else if (its <= 2) SQ_B(2);
         else if (its <= 4) SQ_B(4);
@@ -314,8 +334,8 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
 #define SQ_Q(ITS, LDS)                                                                     \
-    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS><<<grid, block, shmem, stream>>>(         \
-        xv, rows, K, mul, static_scale, q, scale, (int)rpw)
+    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW><<<grid, block, shmem, stream>>>( \
+        xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw)
 #define SQ_QL(ITS) \
     do { if (mul_lds) SQ_Q(ITS, true); else SQ_Q(ITS, false); } while (0)
     switch (its) {
@@ -331,7 +351,13 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
 
 template <int DT>
 static void launch_dt(const void *x, int64_t rows, int64_t K, const float *mul, int dynamic,
-                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream) {
+                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream,
+                      const float *row_mul) {
+    if (row_mul) {  // weights only: per-row steps
+        if (mul) launch_q<DT, true, true, true>(x, rows, K, mul, static_scale, q, scale, stream, row_mul);
+        else launch_q<DT, false, true, true>(x, rows, K, mul, static_scale, q, scale, stream, row_mul);
+        return;
+    }
     if (mul) {
         if (dynamic) launch_q<DT, true, true>(x, rows, K, mul, static_scale, q, scale, stream);
         else launch_q<DT, true, false>(x, rows, K, mul, static_scale, q, scale, stream);
@@ -343,15 +369,15 @@ static void launch_dt(const void *x, int64_t rows, int64_t K, const float *mul, 
 
 void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
                        int dynamic, const float *static_scale, int8_t *q, float *scale,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float *row_mul) {
     if (rows == 0) {
         if (!dynamic)  // the per-tensor step is still reported
             launch_copy_f32(static_scale, scale, stream);
         return;
     }
-    if (dt == F32) launch_dt<F32>(x, rows, K, mul, dynamic, static_scale, q, scale, stream);
-    else if (dt == F16) launch_dt<F16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream);
-    else launch_dt<BF16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream);
+    if (dt == F32) launch_dt<F32>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
+    else if (dt == F16) launch_dt<F16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
+    else launch_dt<BF16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
 }
 
 }  // namespace sq

@@ -60,7 +60,7 @@ const char *sq_status_str(int status) {
     }
 }
 
-int sq_version(void) { return 101; }
+int sq_version(void) { return 102; }
 
 int sq_absmax_reduce(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
                      float *amax_out, void *stream) {
@@ -96,6 +96,19 @@ int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K, const float *
     if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(w_scale, 4))
         return SQ_ERR_ALIGN;
     sq::launch_quant_rows(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream));
+    return finish();
+}
+
+int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K, const float *row_mul,
+                             const float *s, int8_t *wq, float *w_scale, void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (N == 0) return SQ_OK;
+    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(row_mul, 4) ||
+        !aligned(w_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_quant_rows(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream), row_mul);
     return finish();
 }
 

@@ -14,12 +14,13 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
 void launch_compute_scales(const float *act_amax, const float *w_amax, int64_t K, float alpha,
                            float *s, float *inv_s, float *static_scale, hipStream_t stream);
 
-// Per-row quantization of fp(x) * mul (mul may be NULL): a3 uses it with
-// per_row = true for weights, a4 for activations (either mode), a6 for the
-// outlier-masked rows.
+// Per-row quantization of fl(fl(x * row_mul[r]) * mul[k]) (row_mul and mul
+// may be NULL; row_mul only with dynamic steps): a3 uses it for weights
+// (row_mul: the next layer's folded 1/s), a4 for activations (either mode),
+// a6 for the outlier-masked rows.
 void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
                        int dynamic, const float *static_scale, int8_t *q, float *scale,
-                       hipStream_t stream);
+                       hipStream_t stream, const float *row_mul = nullptr);
 
 struct SideTerm {  // LLM.int8() fp16 side product over outlier columns
     const uint16_t *x16;   // [M, K]
