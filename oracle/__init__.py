@@ -75,6 +75,16 @@ def lib():
             "orc_matmul_f64": (None, [_P, _I, _P, _I, _I64, _I64, _I64, _P]),
             "orc_smoothed_matmul_f64": (None, [_P, _I, _P, _I, _P, _I64, _I64, _I64, _P]),
             "orc_fold_norm": (None, [_P, _P, _P, _I64, _P, _P]),
+            "orc_fp8_decode": (_F, [ctypes.c_uint8]),
+            "orc_fp8_encode": (ctypes.c_uint8, [_F]),
+            "orc_quantize_rows_fp8": (None, [_P, _I64, _I64, _P, _P]),
+            "orc_smooth_weights_fp8": (None, [_P, _I, _I64, _I64, _P, _P, _P]),
+            "orc_quantize_act_fp8": (None, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P]),
+            "orc_static_scale": (None, [_P, _P, _I64, _F, _P]),
+            "orc_gemm_fp8_dequant": (None, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P,
+                                            _P]),
+            "orc_gemm_fp8_dequant_at": (None, [_P, _P, _I64, _P, _I, _P, _I, _P, _P, _I64, _P,
+                                               _P, _P]),
             "orc_norm_stats": (None, [_P, _I64, _I64, _I, _F, _P, _P]),
             "orc_norm_quantize": (None, [_P, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
         }
@@ -358,3 +368,98 @@ def norm_quantize(x_f16, gamma, beta=None, norm=NORM_LAYER, eps=1e-5,
     lib().orc_norm_quantize(_ptr(xb), M, K, norm, _ptr(gamma), _ptr(beta), eps, mode,
                             _ptr(st), _ptr(xq), _ptr(xs), _ptr(y))
     return (xq, xs, y) if want_y else (xq, xs)
+
+
+# ------------------------------------------------------------ FP8 (e4m3)
+
+def fp8_decode(codes):
+    """uint8 e4m3fn codes -> float32 values (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, np.uint8)
+    table = np.array([lib().orc_fp8_decode(i) for i in range(256)], np.float32)
+    return table[c]
+
+
+def fp8_encode(v):
+    """float32 values with |v| <= 448 -> e4m3fn codes (nearest, ties even)."""
+    v = np.asarray(v, np.float32)
+    f = lib().orc_fp8_encode
+    return np.array([f(float(t)) for t in v.reshape(-1)], np.uint8).reshape(v.shape)
+
+
+def quantize_rows_fp8(v):
+    v = _c(v.astype(np.float32, copy=False))
+    R, K = v.shape
+    q = np.empty((R, K), np.uint8)
+    step = np.empty(R, np.float32)
+    lib().orc_quantize_rows_fp8(v.ctypes.data, R, K, q.ctypes.data, step.ctypes.data)
+    return q, step
+
+
+def smooth_weights_fp8(w, s=None):
+    w = _c(w)
+    N, K = w.shape
+    wq = np.empty((N, K), np.uint8)
+    ws = np.empty(N, np.float32)
+    if s is not None:
+        s = _c(s.astype(np.float32, copy=False))
+    lib().orc_smooth_weights_fp8(w.ctypes.data, _dt(w), N, K, _ptr(s), wq.ctypes.data,
+                                 ws.ctypes.data)
+    return wq, ws
+
+
+def quantize_act_fp8(x, inv_s=None, mode=PER_TOKEN_DYNAMIC, static_scale=None):
+    x = _c(x)
+    M, K = x.shape
+    xq = np.empty((M, K), np.uint8)
+    xs = np.empty(M if mode == PER_TOKEN_DYNAMIC else 1, np.float32)
+    if inv_s is not None:
+        inv_s = _c(inv_s.astype(np.float32, copy=False))
+    if static_scale is not None:
+        static_scale = _c(np.asarray(static_scale, np.float32))
+    lib().orc_quantize_act_fp8(x.ctypes.data, _dt(x), M, K, _ptr(inv_s), mode,
+                               _ptr(static_scale), xq.ctypes.data, xs.ctypes.data)
+    return xq, xs
+
+
+def static_scale(act_amax, inv_s, qmax):
+    act_amax = _c(act_amax.astype(np.float32, copy=False))
+    if inv_s is not None:
+        inv_s = _c(inv_s.astype(np.float32, copy=False))
+    out = np.empty(2, np.float32)
+    lib().orc_static_scale(act_amax.ctypes.data, _ptr(inv_s), act_amax.size, qmax,
+                           out.ctypes.data)
+    return out
+
+
+def gemm_fp8_dequant(xq, wq, x_scale, w_scale, y_dt=F32, per_row=1):
+    """(y, acc, abs_sum): acc the exact fp64 sum, abs_sum = sum |products|."""
+    xq, wq = _c(xq), _c(wq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    x_scale = _c(np.asarray(x_scale, np.float32))
+    w_scale = _c(np.asarray(w_scale, np.float32))
+    y = _out((M, N), y_dt)
+    acc = np.empty((M, N), np.float64)
+    ab = np.empty((M, N), np.float64)
+    lib().orc_gemm_fp8_dequant(xq.ctypes.data, wq.ctypes.data, M, N, K, x_scale.ctypes.data,
+                               per_row, w_scale.ctypes.data, y.ctypes.data, y_dt,
+                               acc.ctypes.data, ab.ctypes.data)
+    return y, acc, ab
+
+
+def gemm_fp8_dequant_at(xq, wq, x_scale, w_scale, rows, cols, y_dt=F32, per_row=1):
+    xq, wq = _c(xq), _c(wq)
+    K = xq.shape[1]
+    x_scale = _c(np.asarray(x_scale, np.float32))
+    w_scale = _c(np.asarray(w_scale, np.float32))
+    rows = _c(np.asarray(rows, np.int64))
+    cols = _c(np.asarray(cols, np.int64))
+    n = rows.size
+    y = _out((n,), y_dt)
+    acc = np.empty(n, np.float64)
+    ab = np.empty(n, np.float64)
+    lib().orc_gemm_fp8_dequant_at(xq.ctypes.data, wq.ctypes.data, K, x_scale.ctypes.data,
+                                  per_row, w_scale.ctypes.data, y_dt, rows.ctypes.data,
+                                  cols.ctypes.data, n, y.ctypes.data, acc.ctypes.data,
+                                  ab.ctypes.data)
+    return y, acc, ab

@@ -499,3 +499,155 @@ void orc_norm_quantize(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
         free(row);
     }
 }
+
+/* ------------------------------------------------ f4: FP8 (e4m3) */
+
+float orc_fp8_decode(uint8_t b) {
+    int e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+    return (b & 0x80) ? -v : v;
+}
+
+uint8_t orc_fp8_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    /* codes 0 .. 126 increase with their value: find lo with
+     * dec(lo) <= a < dec(lo + 1) */
+    int lo = 0, hi = 126;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if ((double)orc_fp8_decode((uint8_t)mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    if ((double)orc_fp8_decode((uint8_t)hi) <= a) lo = hi;
+    if (lo == 126) return sign | 126;
+    double dl = a - (double)orc_fp8_decode((uint8_t)lo);
+    double dh = (double)orc_fp8_decode((uint8_t)(lo + 1)) - a;
+    int c = dl < dh ? lo : dh < dl ? lo + 1 : (lo % 2 == 0 ? lo : lo + 1);
+    return sign | (uint8_t)c;
+}
+
+static uint8_t fp8_clamp_encode(float z) {
+    if (z > 448.0f) z = 448.0f;
+    if (z < -448.0f) z = -448.0f;
+    return orc_fp8_encode(z);
+}
+
+static void quantize_row_fp8(const float *v, int64_t K, uint8_t *q, float *step) {
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float t = fabsf(v[k]);
+        if (t > a) a = t;
+    }
+    if (!(a > 1e-8f)) a = 1e-8f;
+    float inv = 448.0f / a;
+    *step = a / 448.0f;
+    for (int64_t k = 0; k < K; ++k) q[k] = fp8_clamp_encode(v[k] * inv);
+}
+
+void orc_quantize_rows_fp8(const float *v, int64_t rows, int64_t K, uint8_t *q,
+                           float *step) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) quantize_row_fp8(v + r * K, K, q + r * K, &step[r]);
+}
+
+void orc_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K,
+                            const float *s, uint8_t *wq, float *w_scale) {
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) {
+                float v = load_elem(w, dt, n * K + k);
+                row[k] = s ? v * s[k] : v;
+            }
+            quantize_row_fp8(row, K, wq + n * K, &w_scale[n]);
+        }
+        free(row);
+    }
+}
+
+void orc_quantize_act_fp8(const void *x, int dt, int64_t M, int64_t K,
+                          const float *inv_s, int mode, const float *static_scale,
+                          uint8_t *xq, float *x_scale) {
+    if (mode == ORC_PER_TENSOR_STATIC) x_scale[0] = static_scale[0];
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t k = 0; k < K; ++k) {
+                float v = load_elem(x, dt, m * K + k);
+                row[k] = inv_s ? v * inv_s[k] : v;
+            }
+            if (mode == ORC_PER_TOKEN_DYNAMIC) {
+                quantize_row_fp8(row, K, xq + m * K, &x_scale[m]);
+            } else {
+                for (int64_t k = 0; k < K; ++k)
+                    xq[m * K + k] = fp8_clamp_encode(row[k] * static_scale[1]);
+            }
+        }
+        free(row);
+    }
+}
+
+void orc_static_scale(const float *act_amax, const float *inv_s, int64_t K,
+                      float qmax, float *out) {
+    float a = 0.0f;
+    for (int64_t j = 0; j < K; ++j) {
+        float t = inv_s ? act_amax[j] * inv_s[j] : act_amax[j];
+        if (t > a) a = t;
+    }
+    if (!(a > 1e-8f)) a = 1e-8f;
+    out[0] = a / qmax;
+    out[1] = qmax / a;
+}
+
+static void dot_fp8(const uint8_t *a, const uint8_t *b, int64_t K, double *acc,
+                    double *abs_sum) {
+    double s = 0.0, t = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = (double)orc_fp8_decode(a[k]) * (double)orc_fp8_decode(b[k]);
+        s += p;
+        t += fabs(p);
+    }
+    *acc = s;
+    *abs_sum = t;
+}
+
+void orc_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
+                          int64_t K, const float *x_scale, int per_row,
+                          const float *w_scale, void *y, int y_dt, double *acc_out,
+                          double *abs_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float dx = x_scale[per_row ? m : 0];
+        for (int64_t n = 0; n < N; ++n) {
+            double acc, abs_sum;
+            dot_fp8(xq + m * K, wq + n * K, K, &acc, &abs_sum);
+            if (acc_out) acc_out[m * N + n] = acc;
+            if (abs_out) abs_out[m * N + n] = abs_sum;
+            float c = dx * w_scale[n];
+            if (y) store_elem(y, y_dt, m * N + n, (float)acc * c);
+        }
+    }
+}
+
+void orc_gemm_fp8_dequant_at(const uint8_t *xq, const uint8_t *wq, int64_t K,
+                             const float *x_scale, int per_row, const float *w_scale,
+                             int y_dt, const int64_t *rows, const int64_t *cols,
+                             int64_t n, void *y, double *acc_out, double *abs_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t m = rows[i], c = cols[i];
+        double acc, abs_sum;
+        dot_fp8(xq + m * K, wq + c * K, K, &acc, &abs_sum);
+        if (acc_out) acc_out[i] = acc;
+        if (abs_out) abs_out[i] = abs_sum;
+        float cc = x_scale[per_row ? m : 0] * w_scale[c];
+        if (y) store_elem(y, y_dt, i, (float)acc * cc);
+    }
+}

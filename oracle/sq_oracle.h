@@ -236,4 +236,57 @@ void orc_norm_quantize(const uint16_t *x_f16, int64_t M, int64_t K, int norm,
                        int mode, const float *static_scale, int8_t *xq,
                        float *x_scale, float *y_out);
 
+/* ------------------------------------------------------------------
+ * FP8 (e4m3) variant of the same path.  [SQ-wiki] 技術原理與特性: a
+ * SmoothQuant-quantized model can run on INT8 or FP8 compute units.  The
+ * scale semantics are those of the int8 path with 448, the largest finite
+ * e4m3 value, in place of 127 (reading: the page gives no FP8 details).
+ *
+ * Format (OCP e4m3fn): sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent 0 holds the subnormals m 2^-9; 0x7F and 0xFF are NaN; no
+ * infinities; the largest finite value is 1.75 2^8 = 448.
+ * Pinned: decode of all 256 codes and encode of |v| <= 448 against torch's
+ * float8_e4m3fn conversion; round trip of every finite code; ties. */
+float orc_fp8_decode(uint8_t b);
+/* |v| <= 448 (callers clamp): the nearest e4m3 value, ties to the even
+ * code (the even mantissa). */
+uint8_t orc_fp8_encode(float v);
+
+/* Row quantizer to e4m3: a = max(max_k |v|, 1e-8); step = fl(a / 448);
+ * inv = fl(448 / a); q = encode(clamp(fl(v * inv), -448, 448)).
+ * Pinned: the row maximum lands on +-448; zero rows; the relative
+ * reconstruction error of normal values is at most 2^-4. */
+void orc_quantize_rows_fp8(const float *v, int64_t rows, int64_t K, uint8_t *q,
+                           float *step);
+/* a3 in e4m3: w' = fl(W * s) (s may be NULL), per output channel. */
+void orc_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K,
+                            const float *s, uint8_t *wq, float *w_scale);
+/* a4 in e4m3: xs = fl(X * inv_s) (inv_s may be NULL); PER_TOKEN_DYNAMIC:
+ * the row quantizer above; PER_TENSOR_STATIC: encode(clamp(fl(xs *
+ * static_scale[1]), -448, 448)) and x_scale[0] = static_scale[0]. */
+void orc_quantize_act_fp8(const void *x, int dt, int64_t M, int64_t K,
+                          const float *inv_s, int mode, const float *static_scale,
+                          uint8_t *xq, float *x_scale);
+/* The per-tensor static step for a largest code qmax (127 for int8, 448 for
+ * e4m3): a = max(max_j fl(x_j * inv_s_j), 1e-8) (inv_s may be NULL);
+ * out = {fl(a / qmax), fl(qmax / a)}. */
+void orc_static_scale(const float *act_amax, const float *inv_s, int64_t K,
+                      float qmax, float *out);
+/* e4m3 GEMM: acc[m, n] = sum_k dec(xq[m, k]) dec(wq[n, k]) in double, which
+ * is exact (every product is a multiple of 2^-18 below 2^18, so K <= 2^16
+ * terms need fewer than 53 bits); y = fl(fl32(acc) * fl(dx_m * dw_n)),
+ * narrowed RNE.  acc_out and abs_out (optional, double [M, N]) receive acc
+ * and sum_k |dec(x) dec(w)| (the scale of the fp32 accumulation error a
+ * device accumulator may add).
+ * Pinned: acc against numpy's fp64 product on integer-valued codes. */
+void orc_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
+                          int64_t K, const float *x_scale, int per_row,
+                          const float *w_scale, void *y, int y_dt, double *acc_out,
+                          double *abs_out);
+/* The same at the n (row, col) pairs given (large shapes, sampled). */
+void orc_gemm_fp8_dequant_at(const uint8_t *xq, const uint8_t *wq, int64_t K,
+                             const float *x_scale, int per_row, const float *w_scale,
+                             int y_dt, const int64_t *rows, const int64_t *cols,
+                             int64_t n, void *y, double *acc_out, double *abs_out);
+
 #endif
