@@ -8,6 +8,7 @@
  *   [SQ-practice] "大模型量化困局与SmoothQuant的破局思路" (lpnh.cn)
  *   [SQ-ondevice] "如何通过 SmoothQuant 解决激活值离群点难题" (tbr8.org)
  *   [INT8-expl]   LLM.int8() explainer (xdnf.cn)
+ *   [SQ-wiki]     "SmoothQuant" encyclopedia entry (newton.com.tw)
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers owned by the caller (allocated with
@@ -149,6 +150,54 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
 int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K,
                              const float *row_mul, const float *s, int8_t *wq,
                              float *w_scale, void *stream);
+
+/*
+ * Per-tensor static step for a largest code qmax: a = max(max_j
+ * fl(act_amax_j * inv_s_j), 1e-8) (inv_s NULL: act_amax_j), static_scale =
+ * {fl(a / qmax), fl(qmax / a)}.  qmax = 127 gives a2's int8 step, 448 the
+ * e4m3 one.  [SQ-practice] §7.3 (static steps fixed after calibration).
+ *   act_amax [K], inv_s [K] or NULL, static_scale [2] out; qmax > 0 finite.
+ */
+int sq_static_scale(const float *act_amax, const float *inv_s, int64_t K, float qmax,
+                    float *static_scale, void *stream);
+
+/*
+ * f4 - the FP8 (OCP e4m3fn) form of a3 and a4.  [SQ-wiki] 技術原理與特性:
+ * the quantized model can use INT8 or FP8 compute units.  Same definitions
+ * as the int8 entry points with 448 (the largest finite e4m3 value) in place
+ * of 127: step = fl(a / 448), q = e4m3(clamp(fl(v * fl(448 / a)), -448, 448)),
+ * rounding to nearest even; codes are bytes (sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; 0x7F / 0xFF are NaN and never produced).
+ *   sq_smooth_weights_fp8: w [N, K] of dt, s [K] or NULL -> wq [N, K] e4m3,
+ *                          w_scale [N].
+ *   sq_quantize_act_fp8:   x [M, K] of dt, inv_s [K] or NULL, mode and
+ *                          static_scale as sq_quantize_act (the static pair
+ *                          from sq_static_scale with qmax 448) -> xq [M, K]
+ *                          e4m3, x_scale [M] or [1].
+ * K % 16 == 0.
+ */
+int sq_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K, const float *s,
+                          uint8_t *wq, float *w_scale, void *stream);
+int sq_quantize_act_fp8(const void *x, int dt, int64_t M, int64_t K, const float *inv_s,
+                        int mode, const float *static_scale, uint8_t *xq, float *x_scale,
+                        void *stream);
+
+/*
+ * f4 - e4m3 x e4m3 GEMM on the matrix cores' FP8 path ([SQ-wiki]
+ * 技術原理與特性: INT8 or FP8 units) with a5's dequant epilogue.
+ *   xq [M, K] e4m3, wq [N, K] e4m3 (from the _fp8 quantizers)
+ *   x_scale, x_scale_per_row, w_scale, y, y_dt as sq_gemm_i8_dequant:
+ *   y = fl(acc * fl(x_scale[m] * w_scale[n])) narrowed RNE, where acc is
+ *   sum_k dec(xq[m,k]) dec(wq[n,k]) as the matrix cores form it: products
+ *   are exact, each block of 64 consecutive k is aligned to its largest
+ *   product with limited precision below it, and the blocks are added in
+ *   fp32 (|acc - exact| <= 2^-9 sum_blocks max|p| + K 2^-24 sum|p|,
+ *   measured well inside on this GPU).  Results are deterministic.
+ * K % 128 == 0 (K > 0).
+ */
+int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
+                        int64_t K, const float *x_scale, int x_scale_per_row,
+                        const float *w_scale, void *y, int y_dt, void *stream);
 
 /*
  * a5 - int8 x int8 -> int32 GEMM with the outer-product dequant epilogue.

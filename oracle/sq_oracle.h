@@ -275,18 +275,20 @@ void orc_static_scale(const float *act_amax, const float *inv_s, int64_t K,
 /* e4m3 GEMM: acc[m, n] = sum_k dec(xq[m, k]) dec(wq[n, k]) in double, which
  * is exact (every product is a multiple of 2^-18 below 2^18, so K <= 2^16
  * terms need fewer than 53 bits); y = fl(fl32(acc) * fl(dx_m * dw_n)),
- * narrowed RNE.  acc_out and abs_out (optional, double [M, N]) receive acc
- * and sum_k |dec(x) dec(w)| (the scale of the fp32 accumulation error a
- * device accumulator may add).
+ * narrowed RNE.  Optional double [M, N] outputs for judging a device sum
+ * that is not exact: acc_out = acc, abs_out = sum_k |p_k|, blk_out = the sum
+ * over consecutive 64-term blocks of k of the block's largest |p_k| (the
+ * matrix cores align each block of products to its largest term).
  * Pinned: acc against numpy's fp64 product on integer-valued codes. */
 void orc_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
                           int64_t K, const float *x_scale, int per_row,
                           const float *w_scale, void *y, int y_dt, double *acc_out,
-                          double *abs_out);
+                          double *abs_out, double *blk_out);
 /* The same at the n (row, col) pairs given (large shapes, sampled). */
 void orc_gemm_fp8_dequant_at(const uint8_t *xq, const uint8_t *wq, int64_t K,
                              const float *x_scale, int per_row, const float *w_scale,
                              int y_dt, const int64_t *rows, const int64_t *cols,
-                             int64_t n, void *y, double *acc_out, double *abs_out);
+                             int64_t n, void *y, double *acc_out, double *abs_out,
+                             double *blk_out);
 
 #endif

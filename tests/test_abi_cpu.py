@@ -18,11 +18,11 @@ FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced on these p
 def test_exports_every_declared_symbol():
     L = sq.lib()
     declared = sq.header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(L, name), name
         assert name in sq.SIGNATURES, name
-    assert L.sq_version() == 102
+    assert L.sq_version() == 103
 
 
 def test_status_strings():
@@ -150,3 +150,29 @@ def test_norm_quantize_validation():
     assert f(FAKE, sq.SQ_F16, 4, 64, 0, FAKE, None, 1e-5, 0, None, FAKE, FAKE, None) == NULL
     assert f(FAKE, sq.SQ_F16, 4, 64, 1, FAKE, FAKE + 4, 1e-5, 1, None, FAKE, FAKE, None) == ALIGN
     assert f(FAKE, sq.SQ_F16, 0, 64, 0, FAKE, None, 1e-5, 1, None, FAKE, FAKE, None) == OK
+
+
+def test_fp8_validation():
+    L = sq.lib()
+    assert L.sq_static_scale(FAKE, None, 8, 0.0, FAKE, None) == ARG
+    assert L.sq_static_scale(FAKE, None, 8, float("inf"), FAKE, None) == ARG
+    assert L.sq_static_scale(FAKE, None, -1, 448.0, FAKE, None) == SHAPE
+    assert L.sq_static_scale(None, None, 8, 448.0, FAKE, None) == NULL
+    assert L.sq_static_scale(FAKE + 2, None, 8, 448.0, FAKE, None) == ALIGN
+    assert L.sq_smooth_weights_fp8(FAKE, sq.SQ_F16, 8, 24, None, FAKE, FAKE, None) == SHAPE
+    assert L.sq_smooth_weights_fp8(FAKE, 9, 8, 32, None, FAKE, FAKE, None) == DTYPE
+    assert L.sq_smooth_weights_fp8(FAKE, sq.SQ_F16, 8, 32, None, None, FAKE, None) == NULL
+    assert L.sq_smooth_weights_fp8(None, sq.SQ_F16, 0, 32, None, None, None, None) == OK
+    assert L.sq_quantize_act_fp8(FAKE, sq.SQ_F16, 8, 32, None, 2, None, FAKE, FAKE, None) == ARG
+    assert L.sq_quantize_act_fp8(FAKE, sq.SQ_F16, 8, 32, None, sq.SQ_PER_TENSOR_STATIC, None,
+                                 FAKE, FAKE, None) == NULL
+    assert L.sq_quantize_act_fp8(FAKE, sq.SQ_F16, 8, 32, None, 1, None, FAKE + 8, FAKE,
+                                 None) == ALIGN
+    assert L.sq_quantize_act_fp8(None, sq.SQ_F16, 0, 32, None, 1, None, None, None, None) == OK
+    g = L.sq_gemm_fp8_dequant
+    assert g(FAKE, FAKE, 4, 4, 64, FAKE, 1, FAKE, FAKE, sq.SQ_F16, None) == SHAPE   # K % 128
+    assert g(FAKE, FAKE, 4, 4, 0, FAKE, 1, FAKE, FAKE, sq.SQ_F16, None) == SHAPE
+    assert g(FAKE, FAKE, 4, 4, 128, FAKE, 1, FAKE, FAKE, 7, None) == DTYPE
+    assert g(FAKE, None, 4, 4, 128, FAKE, 1, FAKE, FAKE, sq.SQ_F16, None) == NULL
+    assert g(FAKE, FAKE, 4, 4, 128, FAKE, 1, FAKE, FAKE + 1, sq.SQ_F16, None) == ALIGN
+    assert g(None, None, 0, 4, 128, None, 1, None, None, sq.SQ_F16, None) == OK

@@ -1,0 +1,201 @@
+"""GPU parity of the FP8 (OCP e4m3fn) variant against the CPU oracle on the
+same seeded inputs.  The SmoothQuant encyclopedia page (newton.com.tw),
+section 技術原理與特性: the quantized model can run on INT8 or FP8 units.
+
+Bars: the e4m3 codes and the per-row / per-tensor steps bit-exact (the
+hardware conversion rounds to nearest even, like the oracle's encoder, on
+the clamped values).  The GEMM's sum is the matrix cores': each
+v_mfma_f32_32x32x64_f8f6f4 aligns its block of 64 products to the largest
+one and keeps a limited number of bits below it (measured on this GPU: the
+error of a block stays below 2^-11.5 of its largest product), and the
+blocks are added in fp32.  It is held to the exact sum (the oracle's, in
+fp64) within
+    |acc - exact| <= 2^-9 sum_blocks max|p| + K 2^-24 sum|p|,
+then the reference's rounding of the exact sum to fp32, the two dequant
+products' roundings and the output's:
+    |y - fl(fl32(exact) * c)| <= |c| (that bound) + (2^-22 + u_out) |y_ref|
+with u_out the output's half ulp (0, 2^-11, 2^-8 for fp32, fp16, bf16).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w8a8_post_quantization_amd as sq
+from tests.gpu_util import assert_bits_equal, dev, host, log, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+
+    if not _t.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    sq.lib()
+    return _t
+
+
+def _inputs(dt, shape, seed, stream=1, scale=1.0, outliers=0):
+    a = synth.normal(seed, stream, shape) * np.float32(scale)
+    if outliers:
+        cols = synth.choose(seed, stream + 1, shape[1], outliers)
+        a[:, cols] *= np.float32(40.0)
+    if dt == "f32":
+        return a
+    if dt == "f16":
+        return a.astype(np.float16)
+    return to_bf16_bits(a)
+
+
+def _pos(seed, stream, n):
+    return (np.abs(synth.normal(seed, stream, (n,))) * 2 + 0.05).astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K,dt,with_s", [
+    (3072, 1024, "f16", True), (2100, 2048, "f16", True), (2500, 96, "f32", True),
+    (1000, 4096, "bf16", True), (37, 2064, "f16", False), (50, 16400, "f16", True),
+    (0, 64, "f16", True)])
+def test_smooth_weights_fp8_parity(torch, N, K, dt, with_s):
+    w = _inputs(dt, (N, K), N + K, scale=0.03)
+    s = _pos(N + K, 3, K) if with_s else None
+    log(f"smooth_weights_fp8 N={N} K={K} {dt} s={with_s}")
+    wq, ws = sq.smooth_weights_fp8(dev(w, torch), None if s is None else dev(s, torch))
+    wq_o, ws_o = oracle.smooth_weights_fp8(w, s)
+    assert_bits_equal(host(ws, torch), ws_o, "w_scale")
+    assert_bits_equal(host(wq, torch), wq_o, "wq")
+
+
+@pytest.mark.parametrize("M,K,dt,mode,with_s", [
+    (256, 7168, "f16", 1, True), (4097, 4096, "f16", 1, True), (16, 1024, "f32", 0, True),
+    (33, 3072, "bf16", 0, True), (300, 68 - 68 % 16, "f32", 1, False), (5, 16384, "f16", 1, True),
+    (2049, 2064, "f16", 0, False), (0, 64, "f16", 0, True), (0, 64, "f16", 1, True)])
+def test_quantize_act_fp8_parity(torch, M, K, dt, mode, with_s):
+    x = _inputs(dt, (M, K), M * 7 + K, outliers=max(1, K // 200))
+    inv_s = _pos(M + K, 4, K) if with_s else None
+    st = None
+    if mode == 0:
+        # a tight step so that some values clamp at +-448
+        xa = oracle.absmax_cols(x) if M else np.ones(K, np.float32)
+        st = oracle.static_scale(xa * np.float32(0.25), inv_s, 448.0)
+    log(f"quantize_act_fp8 M={M} K={K} {dt} mode={mode} s={with_s}")
+    xq, xs = sq.quantize_act_fp8(dev(x, torch), None if inv_s is None else dev(inv_s, torch),
+                                 mode, None if st is None else dev(st, torch))
+    xq_o, xs_o = oracle.quantize_act_fp8(x, inv_s, mode, st)
+    assert_bits_equal(host(xs, torch), xs_o, "x_scale")
+    assert_bits_equal(host(xq, torch), xq_o, "xq")
+    if mode == 0 and M:
+        codes = host(xq, torch)
+        assert ((codes & 0x7F) == 0x7E).any()  # clamped at 448
+
+
+@pytest.mark.parametrize("qmax,with_s", [(448.0, True), (448.0, False), (127.0, True)])
+def test_static_scale_parity(torch, qmax, with_s):
+    xa = _pos(5, 6, 3000) * np.float32(10)
+    inv_s = _pos(5, 7, 3000) if with_s else None
+    log(f"static_scale qmax={qmax} s={with_s}")
+    got = sq.static_scale(dev(xa, torch), None if inv_s is None else dev(inv_s, torch), qmax)
+    assert_bits_equal(host(got, torch), oracle.static_scale(xa, inv_s, qmax), "static step")
+
+
+def _codes(seed, shape, spread=1.0):
+    """Random finite e4m3 codes: encode of N(0, spread) values (|v| <= 448)."""
+    v = np.clip(synth.normal(seed, 9, shape) * np.float32(spread), -448, 448)
+    return oracle.fp8_encode(v)
+
+
+def _check_gemm(y, ydt, xs, ws, acc, ab, bs, per_row, K, rows=None, cols=None):
+    """y (host) against the exact sums acc with the accumulation bound."""
+    acc_bound = 2.0 ** -9 * bs + K * 2.0 ** -24 * ab
+    if rows is None:
+        dx = xs[:, None] if per_row else xs[0]
+        c = (np.float32(1) * dx * ws[None, :]).astype(np.float32)
+    else:
+        c = (xs[rows] if per_row else xs[0]) * ws[cols]
+        c = c.astype(np.float32)
+    ref = (acc.astype(np.float32) * c).astype(np.float64)
+    yf = _to_f64(y, ydt)
+    u_out = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[ydt]
+    tol = np.abs(c) * acc_bound + (2.0 ** -22 + u_out) * np.abs(ref) + 1e-30
+    if ydt == "f16":
+        tol = tol + 2.0 ** -25  # fp16 subnormal spacing near zero
+    err = np.abs(yf - ref)
+    bad = np.nonzero(err > tol)
+    assert bad[0].size == 0, (f"{bad[0].size} outputs off; worst ratio "
+                              f"{(err / tol).max():.3f} at {tuple(b[0] for b in bad)}")
+    return float((err / np.maximum(tol, 1e-30)).max())
+
+
+def _to_f64(y, ydt):
+    if ydt == "bf16":
+        return (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return y.astype(np.float64)
+
+
+YDT = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}
+
+
+@pytest.mark.parametrize("M,N,K,ydt,per_row,tile", [
+    (64, 256, 128, "f32", True, None), (300, 520, 1024, "f32", True, None),
+    (1, 4096, 1024, "f16", False, None), (33, 1000, 256, "bf16", True, None),
+    (257, 384, 2048, "f32", True, "0"), (513, 640, 1024, "f16", True, "1"),
+    (200, 300, 512, "f32", False, "2"), (8, 28672 // 8, 8192, "f16", True, None)])
+def test_gemm_fp8_parity(torch, M, N, K, ydt, per_row, tile):
+    xq = _codes(M * 3 + K, (M, K), 2.0)
+    wq = _codes(N * 5 + K, (N, K), 0.5)
+    rng = np.random.default_rng(M + N + K)
+    xs = (rng.random(M if per_row else 1) * 0.02 + 1e-3).astype(np.float32)
+    ws = (rng.random(N) * 0.002 + 1e-5).astype(np.float32)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[ydt]
+    if tile is not None:
+        os.environ["SQ_GEMM_TILE"] = tile
+    try:
+        log(f"gemm_fp8 M={M} N={N} K={K} y={ydt} per_row={per_row} tile={tile}")
+        y = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                                out_dtype=tdt)
+        y2 = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                                 out_dtype=tdt)
+    finally:
+        os.environ.pop("SQ_GEMM_TILE", None)
+    _, acc, ab, bs = oracle.gemm_fp8_dequant(xq, wq, xs, ws, y_dt=YDT[ydt],
+                                             per_row=int(per_row))
+    worst = _check_gemm(host(y, torch), ydt, xs, ws, acc, ab, bs, per_row, K)
+    assert_bits_equal(host(y2, torch), host(y, torch), "y rerun (deterministic)")
+    print(f"\ngemm_fp8 M={M} N={N} K={K}: worst error / bound {worst:.3f}")
+
+
+def test_fp8_layer_prefill_full_size(torch):
+    """The prefill layer (X fp16 [256,7168], W fp16 [28672,7168], alpha 0.5,
+    per-token) through the e4m3 path: codes and steps bit-exact at full size,
+    the GEMM checked on a sample of outputs; its error against the fp64
+    product is reported next to the int8 path's."""
+    cfg = synth.prefill_30b()
+    X, W = cfg["X"], cfg["W"]
+    xa, wa = oracle.absmax_cols(X), oracle.absmax_cols(W)
+    s_o, inv_o = oracle.compute_scales(xa, wa, 0.5)
+    log("fp8 prefill weights")
+    wq, ws = sq.smooth_weights_fp8(dev(W, torch), dev(s_o, torch))
+    wq_o, ws_o = oracle.smooth_weights_fp8(W, s_o)
+    assert_bits_equal(host(ws, torch), ws_o, "w_scale")
+    assert_bits_equal(host(wq, torch), wq_o, "wq")
+    log("fp8 prefill activations")
+    xq, xs = sq.quantize_act_fp8(dev(X, torch), dev(inv_o, torch))
+    xq_o, xs_o = oracle.quantize_act_fp8(X, inv_o)
+    assert_bits_equal(host(xs, torch), xs_o, "x_scale")
+    assert_bits_equal(host(xq, torch), xq_o, "xq")
+    log("fp8 prefill gemm")
+    y = host(sq.gemm_fp8_dequant(xq, wq, xs, ws, out_dtype=torch.float32), torch)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, X.shape[0], 4096)
+    cols = rng.integers(0, W.shape[0], 4096)
+    _, acc, ab, bs = oracle.gemm_fp8_dequant_at(xq_o, wq_o, xs_o, ws_o, rows, cols)
+    worst = _check_gemm(y[rows, cols], "f32", xs_o, ws_o, acc, ab, bs, True, X.shape[1], rows,
+                        cols)
+    ref = oracle.matmul_f64(X[:64], W)
+    err8 = np.linalg.norm(y[:64] - ref) / np.linalg.norm(ref)
+    print(f"\nfp8 prefill: worst error / bound {worst:.3f}; rel. error vs fp64 (64 rows) "
+          f"{err8:.4f}")
+    assert err8 < 0.05

@@ -110,21 +110,25 @@ def test_gemm_fp8_exact_sum():
     assert np.array_equal(oracle.fp8_decode(xq), xi)
     xs = rng.uniform(0.01, 0.1, M).astype(np.float32)
     ws = rng.uniform(0.01, 0.1, N).astype(np.float32)
-    y, acc, ab = oracle.gemm_fp8_dequant(xq, wq, xs, ws)
+    y, acc, ab, bs = oracle.gemm_fp8_dequant(xq, wq, xs, ws)
     ref = xi.astype(np.float64) @ wi.astype(np.float64).T
     assert np.array_equal(acc, ref)
     assert np.array_equal(ab, np.abs(xi).astype(np.float64) @ np.abs(wi).astype(np.float64).T)
+    P = np.abs(xi.astype(np.float64)[:, None, :] * wi.astype(np.float64)[None, :, :])
+    blocks = [P[..., k:k + 64].max(-1) for k in range(0, K, 64)]   # K = 320: 5 blocks
+    assert np.array_equal(bs, np.sum(blocks, axis=0))
     c = xs[:, None] * ws[None, :]
     assert np.array_equal(y, acc.astype(np.float32) * c)
     # the sampled form gives the same values
     rows, cols = np.array([0, 3, 6]), np.array([8, 0, 4])
-    y2, acc2, _ = oracle.gemm_fp8_dequant_at(xq, wq, xs, ws, rows, cols)
+    y2, acc2, _, bs2 = oracle.gemm_fp8_dequant_at(xq, wq, xs, ws, rows, cols)
+    assert np.array_equal(bs2, bs[rows, cols])
     assert np.array_equal(acc2, acc[rows, cols]) and np.array_equal(y2, y[rows, cols])
     # the largest and the smallest products together stay exact
     xq2 = np.array([[0x7E, 0x01, 0xFE, 0x01]], np.uint8)    # 448, 2^-9, -448, 2^-9
     wq2 = np.array([[0x7E, 0x01, 0x7E, 0x81]], np.uint8)    # 448, 2^-9, 448, -2^-9
     one = np.ones(1, np.float32)
-    _, acc3, ab3 = oracle.gemm_fp8_dequant(xq2[:, :2], wq2[:, :2], one, one)
+    _, acc3, ab3, _ = oracle.gemm_fp8_dequant(xq2[:, :2], wq2[:, :2], one, one)
     assert acc3[0, 0] == 448.0 ** 2 + 2.0 ** -18 and acc3[0, 0] != 448.0 ** 2
-    _, acc4, ab4 = oracle.gemm_fp8_dequant(xq2, wq2, one, one)
+    _, acc4, ab4, _ = oracle.gemm_fp8_dequant(xq2, wq2, one, one)
     assert acc4[0, 0] == 0.0 and ab4[0, 0] == 2 * (448.0 ** 2 + 2.0 ** -18)

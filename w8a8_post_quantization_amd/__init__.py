@@ -52,6 +52,10 @@ SIGNATURES = {
                                   _P, _I, _P, _P]),
     "sq_fold_norm": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "sq_norm_quantize_act": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
+    "sq_static_scale": (_I, [_P, _P, _I64, _F, _P, _P]),
+    "sq_smooth_weights_fp8": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P]),
+    "sq_quantize_act_fp8": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _P]),
+    "sq_gemm_fp8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P]),
 }
 
 
@@ -288,3 +292,74 @@ def norm_quantize_act(x, gamma, beta=None, norm=SQ_NORM_LAYER, eps=1e-5,
           _ptr(beta), float(eps), int(mode), _ptr(static_scale), xq.data_ptr(), xs.data_ptr(),
           _stream(stream))
     return xq, xs
+
+
+# ------------------------------------------------------------ FP8 (e4m3)
+
+def static_scale(act_amax, inv_s=None, qmax=127.0, stream=None):
+    """{step, 1/step} of a per-tensor static activation step (qmax 127 for
+    int8, 448 for e4m3)."""
+    torch = _torch()
+    _check(act_amax, "act_amax", (torch.float32,), 1)
+    if inv_s is not None:
+        _check(inv_s, "inv_s", (torch.float32,), 1)
+    out = torch.empty(2, dtype=torch.float32, device=act_amax.device)
+    _call("sq_static_scale", act_amax.data_ptr(), _ptr(inv_s), act_amax.numel(), float(qmax),
+          out.data_ptr(), _stream(stream))
+    return out
+
+
+def smooth_weights_fp8(w, s=None, stream=None):
+    """a3 in e4m3: (wq uint8 [N,K] e4m3 codes, w_scale fp32 [N])."""
+    torch = _torch()
+    _check(w, "w", (torch.float32, torch.float16, torch.bfloat16), 2)
+    if s is not None:
+        _check(s, "s", (torch.float32,), 1)
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    ws = torch.empty(N, dtype=torch.float32, device=w.device)
+    _call("sq_smooth_weights_fp8", w.data_ptr(), _dt(w), N, K, _ptr(s), wq.data_ptr(),
+          ws.data_ptr(), _stream(stream))
+    return wq, ws
+
+
+def quantize_act_fp8(x, inv_s=None, mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, stream=None):
+    """a4 in e4m3: (xq uint8 [M,K] e4m3 codes, x_scale fp32 [M] or [1])."""
+    torch = _torch()
+    x2 = x.reshape(-1, x.shape[-1])
+    _check(x2, "x", (torch.float32, torch.float16, torch.bfloat16))
+    if inv_s is not None:
+        _check(inv_s, "inv_s", (torch.float32,), 1)
+    if static_scale is not None:
+        _check(static_scale, "static_scale", (torch.float32,), 1)
+    M, K = x2.shape
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    xs = torch.empty(M if mode == SQ_PER_TOKEN_DYNAMIC else 1, dtype=torch.float32,
+                     device=x.device)
+    _call("sq_quantize_act_fp8", x2.data_ptr(), _dt(x2), M, K, _ptr(inv_s), int(mode),
+          _ptr(static_scale), xq.data_ptr(), xs.data_ptr(), _stream(stream))
+    return xq, xs
+
+
+def gemm_fp8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, out=None, stream=None):
+    """f4: y [M,N] = fl(acc * fl(x_scale * w_scale)) with acc the fp32 sum of
+    the e4m3 products (K % 128 == 0)."""
+    torch = _torch()
+    _check(xq, "xq", (torch.uint8,), 2)
+    _check(wq, "wq", (torch.uint8,), 2)
+    _check(x_scale, "x_scale", (torch.float32,), 1)
+    _check(w_scale, "w_scale", (torch.float32,), 1)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)}, wq {tuple(wq.shape)}")
+    per_row = 1 if (x_scale.numel() == M and M != 1) else 0
+    if not per_row and x_scale.numel() != 1:
+        raise ValueError(f"x_scale has {x_scale.numel()} elements for M = {M}")
+    if w_scale.numel() != N:
+        raise ValueError(f"w_scale has {w_scale.numel()} elements for N = {N}")
+    dt = out_dtype or torch.float16
+    y = out if out is not None else torch.empty((M, N), dtype=dt, device=xq.device)
+    _call("sq_gemm_fp8_dequant", xq.data_ptr(), wq.data_ptr(), M, N, K, x_scale.data_ptr(),
+          int(per_row), w_scale.data_ptr(), y.data_ptr(), _dt(y), _stream(stream))
+    return y

@@ -26,10 +26,15 @@
 // operands; the float epilogue is per element and order-free.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_launch.h"
 
 namespace sq {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int int8x __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -390,9 +395,9 @@ __device__ __forceinline__ void lds_barrier() {
 // holds output column n = 8*(v/4) + 4*(l/32) + (v%4) of n-fragment i and
 // row m = l%32 of m-fragment j: four consecutive columns of one row per
 // group of four registers.
-template <int BM, int BN, int WM, int WN, int YDT, bool SIDE>
+template <int BM, int BN, int WM, int WN, int YDT, bool SIDE, typename AccV>
 __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
-                                            int16v (&acc)[BN / WN / 32][BM / WM / 32],
+                                            AccV (&acc)[BN / WN / 32][BM / WM / 32],
                                             int8_t *smem, const float *sx, const float *sw,
                                             int m0, int n0) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -436,7 +441,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
         }
     }
     // Exact int32 sums, when asked for (direct stores, not on the fast path).
-    if (p.acc_out) {
+    if constexpr (std::is_same_v<AccV, int16v>) if (p.acc_out) {
         const bool vec_a = (N & 3) == 0 && ((uintptr_t)p.acc_out & 15) == 0;
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
@@ -590,7 +595,7 @@ __device__ __forceinline__ void sched_tail() {
 // quarter's MFMAs.  Weight rows are the MFMA A operand (see epilogue_nt).
 // The side-term variant asks for two waves per SIMD: its 128x128 tiles are
 // small, and one wave per SIMD halves how many tiles a CU has in flight.
-template <int BM, int BN, int WM, int WN, int STA, int STB, int YDT, bool SIDE>
+template <int BM, int BN, int WM, int WN, int STA, int STB, int YDT, bool SIDE, bool F8 = false>
 __global__ __launch_bounds__(64 * WM * WN, SIDE ? 2 : 1) __attribute__((amdgpu_waves_per_eu(SIDE ? 2 : 1, 4))) void
 gemm_pp(GemmArgs p) {
     constexpr int BK = 128;
@@ -668,7 +673,8 @@ gemm_pp(GemmArgs p) {
             wf[f] = *reinterpret_cast<const int4v *>(bb + (wn * WTN + f * 32 + fr) * BK);
     };
 
-    int16v acc[FN][FM];
+    using AccV = std::conditional_t<F8, f32x16, int16v>;
+    AccV acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -683,6 +689,67 @@ gemm_pp(GemmArgs p) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[i], xf[j], acc[i][j], 0, 0, 0);
     };
 
+    if constexpr (F8) {
+        // e4m3 operands: one v_mfma_f32_32x32x64_f8f6f4 takes two K quarters
+        // (each lane's 16-byte chunk of quarter q and of quarter q + 1 as one
+        // 32-byte operand).  A and B are built the same way, so the MFMA
+        // sees one consistent permutation of the 64 K values: the sum is the
+        // same set of products.  Quarters 2 and 3 are read while quarters 0
+        // and 1 multiply, and the next stage's 0 and 1 (after the barrier,
+        // with the stage's direct loads) while 2 and 3 multiply.
+        auto mma8 = [&](const int4v (&xa)[FM], const int4v (&wa)[FN], const int4v (&xb)[FM],
+                        const int4v (&wb)[FN]) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int8x a = __builtin_shufflevector(wa[i], wb[i], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const int8x b = __builtin_shufflevector(xa[j], xb[j], 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+                }
+        };
+        if constexpr (STB > STA) {
+#pragma unroll
+            for (int s = 0; s < STB; ++s) issue_b(s);
+#pragma unroll
+            for (int s = 0; s < STA; ++s) issue_a(s);
+            wait_vmcnt<(STA - 1) * LA>();
+        } else {
+#pragma unroll
+            for (int s = 0; s < STA; ++s) {
+                issue_a(s);
+                issue_b(s);
+            }
+            wait_vmcnt<(STA - 1) * L>();
+        }
+        lds_barrier();
+        int4v x0[FM], w0[FN], x1[FM], w1[FN], x2[FM], w2[FN], x3[FM], w3[FN];
+        read_frags(0, 0, x0, w0);
+        read_frags(0, 1, x1, w1);
+        for (int kt = 0; kt < nk; ++kt) {
+            read_frags(kt, 2, x2, w2);
+            read_frags(kt, 3, x3, w3);
+            mma8(x0, w0, x1, w1);
+            if constexpr (STB > STA) {
+                if (kt == 0) wait_vmcnt<0>();
+                else wait_vmcnt<LB>();
+            } else {
+                wait_vmcnt<(STA - 2) * L>();
+            }
+            lds_barrier();  // every wave has read stage kt: its slots are free
+            read_frags(kt + 1, 0, x0, w0);
+            read_frags(kt + 1, 1, x1, w1);
+            issue_a(kt + STA);
+            issue_b(kt + STB);
+            mma8(x2, w2, x3, w3);
+        }
+        wait_vmcnt<0>();
+        scl.publish(sx, sw);
+        __syncthreads();
+        epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0);
+        return;
+    } else {
     // Main loop.  Its two halves are branch-free so the scheduler can
     // interleave: a wave issues in order, so a ds_read (or direct load)
     // queued behind an MFMA that waits for the matrix core cannot issue; the
@@ -747,6 +814,7 @@ gemm_pp(GemmArgs p) {
     scl.publish(sx, sw);
     __syncthreads();  // steps visible; the side term may reuse the ring
     epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0);
+    }
 }
 
 // ---------------------------------------------------------------- decode
@@ -956,14 +1024,14 @@ static void launch_tile_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     else gemm_tile<BM, BN, WM, WN, BF16, SIDE><<<grid, block, 0, stream>>>(a);
 }
 
-template <int BM, int BN, int WM, int WN, int STA, int STB, bool SIDE>
+template <int BM, int BN, int WM, int WN, int STA, int STB, bool SIDE, bool F8 = false>
 static void launch_pipe_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
     a.tiles_n = tn;
     dim3 grid((unsigned)(tm * tn)), block(64 * WM * WN);
-    if (y_dt == F32) gemm_pp<BM, BN, WM, WN, STA, STB, F32, SIDE><<<grid, block, 0, stream>>>(a);
-    else if (y_dt == F16) gemm_pp<BM, BN, WM, WN, STA, STB, F16, SIDE><<<grid, block, 0, stream>>>(a);
-    else gemm_pp<BM, BN, WM, WN, STA, STB, BF16, SIDE><<<grid, block, 0, stream>>>(a);
+    if (y_dt == F32) gemm_pp<BM, BN, WM, WN, STA, STB, F32, SIDE, F8><<<grid, block, 0, stream>>>(a);
+    else if (y_dt == F16) gemm_pp<BM, BN, WM, WN, STA, STB, F16, SIDE, F8><<<grid, block, 0, stream>>>(a);
+    else gemm_pp<BM, BN, WM, WN, STA, STB, BF16, SIDE, F8><<<grid, block, 0, stream>>>(a);
 }
 
 template <int NF, int FT, int U, int S, bool NT>
@@ -1034,6 +1102,29 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         case 0: launch_tile_t<256, 256, 2, 2, false>(a, y_dt, stream); break;
         case 1: launch_tile_t<256, 128, 2, 2, false>(a, y_dt, stream); break;
         default: launch_tile_t<128, 128, 2, 2, false>(a, y_dt, stream); break;
+    }
+}
+
+// e4m3 x e4m3 -> fp32 GEMM with the same dequant epilogue (K % 128 == 0).
+// Every M uses the pipelined kernel (for M <= 32 the 128 x 128 tile, its
+// rows past M clamped to the last one).
+void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
+                     const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
+                     hipStream_t stream) {
+    if (M == 0 || N == 0) return;
+    GemmArgs a{};
+    a.xq = reinterpret_cast<const int8_t *>(xq);
+    a.wq = reinterpret_cast<const int8_t *>(wq);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.xs = x_scale; a.xs_per_row = per_row; a.ws = w_scale; a.y = y;
+    int tile = M <= 32 ? 2 : pick_tile(M, N);
+    if (const char *e = getenv("SQ_GEMM_TILE")) {
+        if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
+    }
+    switch (tile) {
+        case 0: launch_pipe_t<256, 256, 4, 2, 2, 2, false, true>(a, y_dt, stream); break;
+        case 1: launch_pipe_t<256, 128, 4, 2, 3, 3, false, true>(a, y_dt, stream); break;
+        default: launch_pipe_t<128, 128, 2, 2, 2, 2, false, true>(a, y_dt, stream); break;
     }
 }
 

@@ -13,6 +13,11 @@
 //    0/1 column mask; the xdnf.cn explainer §2.2).  Multiplying by 1.0 is
 //    exact and by 0.0 gives +-0, which quantizes to 0, the same as
 //    removing the column.
+// With FP8 = true the codes are OCP e4m3fn instead (448 in place of 127:
+// step = fl(a/448), q = e4m3(clamp(fl(v * fl(448/a)), -448, 448)) by the
+// hardware conversion, which rounds to nearest even and is exact on every
+// in-range value; the SmoothQuant encyclopedia page, 技術原理與特性: INT8 or
+// FP8 units).
 // Weights may also carry a per-row factor applied first,
 // v = fl(fl(x[r, k] * row_mul[r]) * mul[k]): the next layer's 1/s folded
 // into this layer's output channels (the SmoothQuant tutorial page, section
@@ -72,10 +77,35 @@ __device__ __forceinline__ void scaled(const uint4 &raw, const float *__restrict
     }
 }
 
-template <int DT>
+// Four values -> four e4m3 bytes (clamped to the finite range first: the
+// conversion does not saturate).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d, float inv) {
+    const float za = __builtin_amdgcn_fmed3f(a * inv, -448.0f, 448.0f);
+    const float zb = __builtin_amdgcn_fmed3f(b * inv, -448.0f, 448.0f);
+    const float zc = __builtin_amdgcn_fmed3f(c * inv, -448.0f, 448.0f);
+    const float zd = __builtin_amdgcn_fmed3f(d * inv, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(za, zb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(zc, zd, w, true);
+    return (uint32_t)w;
+}
+
+template <bool FP8> struct QMax;
+template <> struct QMax<false> { static constexpr float v = 127.0f; };
+template <> struct QMax<true> { static constexpr float v = 448.0f; };
+
+template <int DT, bool FP8 = false>
 __device__ __forceinline__ void store_q(int8_t *__restrict__ q, int64_t e0, const float *v,
                                         float inv) {
-    if constexpr (Vec<DT>::n == 8) {
+    if constexpr (FP8) {
+        if constexpr (Vec<DT>::n == 8) {
+            uint2 o;
+            o.x = pack_fp8x4(v[0], v[1], v[2], v[3], inv);
+            o.y = pack_fp8x4(v[4], v[5], v[6], v[7], inv);
+            *reinterpret_cast<uint2 *>(q + e0) = o;
+        } else {
+            *reinterpret_cast<uint32_t *>(q + e0) = pack_fp8x4(v[0], v[1], v[2], v[3], inv);
+        }
+    } else if constexpr (Vec<DT>::n == 8) {
         uint2 o;
         o.x = pack4(quant_i8(v[0], inv), quant_i8(v[1], inv), quant_i8(v[2], inv),
                     quant_i8(v[3], inv));
@@ -101,7 +131,7 @@ constexpr int kMulLds = 16384;
 // branch makes the compiler wait for all earlier memory operations first,
 // which would serialize the row's loads.  ITS = 0: rows longer than
 // 16 x 64 vectors, streamed twice (the second pass hits L2).
-template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW>
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW, bool FP8>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
                                                          const float *__restrict__ mul_g,
@@ -155,8 +185,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             }
             a = wave_max(a);
             if (!(a > 1e-8f)) a = 1e-8f;
-            const float inv = 127.0f / a;
-            if (lane == 0) scale[r] = a / 127.0f;
+            const float inv = QMax<FP8>::v / a;
+            if (lane == 0) scale[r] = a / QMax<FP8>::v;
             int8_t *qr = q + r * K;
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
@@ -169,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 if (vi < nvec) {
                     float v[V];
                     scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm);
-                    store_q<DT>(qr, vi * V, v, inv);
+                    store_q<DT, FP8>(qr, vi * V, v, inv);
                 }
             }
         };
@@ -209,18 +239,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             }
             a = wave_max(a);
             if (!(a > 1e-8f)) a = 1e-8f;
-            const float inv = 127.0f / a;
-            if (lane == 0) scale[r] = a / 127.0f;
+            const float inv = QMax<FP8>::v / a;
+            if (lane == 0) scale[r] = a / QMax<FP8>::v;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
-                store_q<DT>(qr, vi * V, v, inv);
+                store_q<DT, FP8>(qr, vi * V, v, inv);
             }
         } else {
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
-                store_q<DT>(qr, vi * V, v, inv_static);
+                store_q<DT, FP8>(qr, vi * V, v, inv_static);
             }
         }
     }
@@ -231,7 +261,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
 // before the reduction; the row maximum is combined across the 4 waves
 // through LDS.  Out-of-range vector indices are clamped to the row's last
 // vector (loaded, not used) so every load is unconditional.
-template <int DT, bool HAS_MUL, bool DYN, int ITS, bool HAS_ROW>
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool HAS_ROW, bool FP8>
 __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__restrict__ x,
                                                               int64_t K,
                                                               const float *__restrict__ mul,
@@ -276,8 +306,8 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
         __syncthreads();
         a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         if (!(a > 1e-8f)) a = 1e-8f;
-        inv = 127.0f / a;
-        if (tid == 0) scale[r] = a / 127.0f;
+        inv = QMax<FP8>::v / a;
+        if (tid == 0) scale[r] = a / QMax<FP8>::v;
     } else {
         inv = static_scale[1];
     }
@@ -296,12 +326,12 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
 #pragma unroll
                 for (int i = 0; i < V; ++i) v[i] = v[i] * m[it][i];
             }
-            store_q<DT>(qr, vi * V, v, inv);
+            store_q<DT, FP8>(qr, vi * V, v, inv);
         }
     }
 }
 
-template <int DT, bool HAS_MUL, bool DYN, bool HAS_ROW = false>
+template <int DT, bool HAS_MUL, bool DYN, bool HAS_ROW = false, bool FP8 = false>
 static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream,
                      const float *row_mul = nullptr) {
@@ -313,7 +343,7 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
         const int64_t its = (nvec + 255) / 256;
         dim3 grid((unsigned)rows), block(256);
 #define SQ_B(ITS) \
-    quant_row_block_kernel<DT, HAS_MUL, DYN, ITS, HAS_ROW><<<grid, block, 0, stream>>>(        \
+    quant_row_block_kernel<DT, HAS_MUL, DYN, ITS, HAS_ROW, FP8><<<grid, block, 0, stream>>>(   \
         xv, K, mul, row_mul, static_scale, q, scale)
         if (its <= 1) SQ_B(1);
         else if (its <= 2) SQ_B(2);
@@ -334,7 +364,7 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
 #define SQ_Q(ITS, LDS)                                                                     \
-    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW><<<grid, block, shmem, stream>>>( \
+    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8><<<grid, block, shmem, stream>>>( \
         xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw)
 #define SQ_QL(ITS) \
     do { if (mul_lds) SQ_Q(ITS, true); else SQ_Q(ITS, false); } while (0)
@@ -347,6 +377,19 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     }
 #undef SQ_QL
 #undef SQ_Q
+}
+
+template <int DT>
+static void launch_dt_fp8(const void *x, int64_t rows, int64_t K, const float *mul, int dynamic,
+                          const float *static_scale, int8_t *q, float *scale,
+                          hipStream_t stream) {
+    if (mul) {
+        if (dynamic) launch_q<DT, true, true, false, true>(x, rows, K, mul, static_scale, q, scale, stream);
+        else launch_q<DT, true, false, false, true>(x, rows, K, mul, static_scale, q, scale, stream);
+    } else {
+        if (dynamic) launch_q<DT, false, true, false, true>(x, rows, K, mul, static_scale, q, scale, stream);
+        else launch_q<DT, false, false, false, true>(x, rows, K, mul, static_scale, q, scale, stream);
+    }
 }
 
 template <int DT>
@@ -365,6 +408,19 @@ static void launch_dt(const void *x, int64_t rows, int64_t K, const float *mul, 
         if (dynamic) launch_q<DT, false, true>(x, rows, K, mul, static_scale, q, scale, stream);
         else launch_q<DT, false, false>(x, rows, K, mul, static_scale, q, scale, stream);
     }
+}
+
+void launch_quant_rows_fp8(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
+                           int dynamic, const float *static_scale, uint8_t *q, float *scale,
+                           hipStream_t stream) {
+    if (rows == 0) {
+        if (!dynamic) launch_copy_f32(static_scale, scale, stream);
+        return;
+    }
+    int8_t *qq = reinterpret_cast<int8_t *>(q);
+    if (dt == F32) launch_dt_fp8<F32>(x, rows, K, mul, dynamic, static_scale, qq, scale, stream);
+    else if (dt == F16) launch_dt_fp8<F16>(x, rows, K, mul, dynamic, static_scale, qq, scale, stream);
+    else launch_dt_fp8<BF16>(x, rows, K, mul, dynamic, static_scale, qq, scale, stream);
 }
 
 void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const float *mul,

@@ -132,14 +132,18 @@ __global__ __launch_bounds__(256) void scales_kernel(const float *__restrict__ a
     inv_s[j] = 1.0f / sj;
 }
 
-// One block: a = max(max_j fl(x_j * inv_s_j), 1e-8); {a/127, 127/a}.
+// One block: a = max(max_j fl(x_j * inv_s_j), 1e-8) (inv_s NULL: x_j);
+// {a/qmax, qmax/a} (qmax 127 for int8 codes, 448 for e4m3).
 __global__ __launch_bounds__(1024) void static_scale_kernel(const float *__restrict__ act_amax,
                                                             const float *__restrict__ inv_s,
-                                                            int64_t K,
+                                                            int64_t K, float qmax,
                                                             float *__restrict__ out) {
     __shared__ float red[16];
     float m = 0.0f;
-    for (int64_t j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, act_amax[j] * inv_s[j]);
+    if (inv_s)
+        for (int64_t j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, act_amax[j] * inv_s[j]);
+    else
+        for (int64_t j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, act_amax[j]);
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(1024) void static_scale_kernel(const float *__restr
         float a = red[0];
         for (int i = 1; i < 16; ++i) a = fmaxf(a, red[i]);
         if (!(a > 1e-8f)) a = 1e-8f;
-        out[0] = a / 127.0f;
-        out[1] = 127.0f / a;
+        out[0] = a / qmax;
+        out[1] = qmax / a;
     }
 }
 
@@ -158,8 +162,13 @@ void launch_compute_scales(const float *act_amax, const float *w_amax, int64_t K
         scales_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream>>>(
             act_amax, w_amax, K, (double)alpha, s, inv_s);
     if (static_scale)
-        static_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(act_amax, inv_s, K,
+        static_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(act_amax, inv_s, K, 127.0f,
                                                                  static_scale);
+}
+
+void launch_static_scale(const float *act_amax, const float *inv_s, int64_t K, float qmax,
+                         float *out, hipStream_t stream) {
+    static_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(act_amax, inv_s, K, qmax, out);
 }
 
 // LLM.int8() outlier list: O = ascending { j : colmax_j >= threshold }

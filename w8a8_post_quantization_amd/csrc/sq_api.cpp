@@ -60,7 +60,7 @@ const char *sq_status_str(int status) {
     }
 }
 
-int sq_version(void) { return 102; }
+int sq_version(void) { return 103; }
 
 int sq_absmax_reduce(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
                      float *amax_out, void *stream) {
@@ -112,6 +112,46 @@ int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K, const 
     return finish();
 }
 
+int sq_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K, const float *s,
+                          uint8_t *wq, float *w_scale, void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (N == 0) return SQ_OK;
+    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(w_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_quant_rows_fp8(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream));
+    return finish();
+}
+
+int sq_quantize_act_fp8(const void *x, int dt, int64_t M, int64_t K, const float *inv_s,
+                        int mode, const float *static_scale, uint8_t *xq, float *x_scale,
+                        void *stream) {
+    if (!valid_dt(dt)) return SQ_ERR_DTYPE;
+    if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
+    if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;
+    if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
+    if (M > 0 && K > 0 && (!x || !xq)) return SQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(inv_s, 16) || !aligned(x_scale, 4) ||
+        !aligned(static_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_quant_rows_fp8(x, dt, M, K, inv_s, mode == SQ_PER_TOKEN_DYNAMIC, static_scale, xq,
+                              x_scale, st(stream));
+    return finish();
+}
+
+int sq_static_scale(const float *act_amax, const float *inv_s, int64_t K, float qmax,
+                    float *static_scale, void *stream) {
+    if (!(qmax > 0.0f) || !(qmax < 3.0e38f)) return SQ_ERR_ARG;
+    if (K < 0 || K > kMaxDim) return SQ_ERR_SHAPE;
+    if (!static_scale || (K > 0 && !act_amax)) return SQ_ERR_NULL;
+    if (!aligned(act_amax, 4) || !aligned(inv_s, 4) || !aligned(static_scale, 4))
+        return SQ_ERR_ALIGN;
+    sq::launch_static_scale(act_amax, inv_s, K, qmax, static_scale, st(stream));
+    return finish();
+}
+
 int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *inv_s, int mode,
                     const float *static_scale, int8_t *xq, float *x_scale, void *stream) {
     if (!valid_dt(dt)) return SQ_ERR_DTYPE;
@@ -142,6 +182,23 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
         return SQ_ERR_ALIGN;
     sq::launch_gemm(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
                     acc_out, nullptr, st(stream));
+    return finish();
+}
+
+int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
+                        const float *x_scale, int x_scale_per_row, const float *w_scale,
+                        void *y, int y_dt, void *stream) {
+    if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 128 != 0)
+        return SQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return SQ_OK;
+    if (K == 0) return SQ_ERR_SHAPE;
+    if (!x_scale || !w_scale || !y || !xq || !wq) return SQ_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+        !aligned(y, esize(y_dt)))
+        return SQ_ERR_ALIGN;
+    sq::launch_gemm_fp8(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
+                        st(stream));
     return finish();
 }
 

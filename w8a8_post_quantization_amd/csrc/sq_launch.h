@@ -22,6 +22,19 @@ void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const flo
                        int dynamic, const float *static_scale, int8_t *q, float *scale,
                        hipStream_t stream, const float *row_mul = nullptr);
 
+// e4m3 codes (OCP e4m3fn), 448 in place of 127; per-row or static steps.
+void launch_quant_rows_fp8(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
+                           int dynamic, const float *static_scale, uint8_t *q, float *scale,
+                           hipStream_t stream);
+// {a/qmax, qmax/a} with a = max(max_j fl(act_amax_j * inv_s_j), 1e-8).
+void launch_static_scale(const float *act_amax, const float *inv_s, int64_t K, float qmax,
+                         float *out, hipStream_t stream);
+
+// e4m3 x e4m3 -> fp32 GEMM, y = fl(acc * fl(dx * dw)); K % 128 == 0.
+void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
+                     const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
+                     hipStream_t stream);
+
 struct SideTerm {  // LLM.int8() fp16 side product over outlier columns
     const uint16_t *x16;   // [M, K]
     const uint16_t *w16;   // [N, K]
