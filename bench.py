@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5033.0      # MI355X dense int8 MFMA (256 CU x 2.4 GHz x 8192 ops/clk)
+PEAK_FP8_TFLOPS = 5033.0     # MI355X dense fp8 MFMA (the same rate per clock)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "W8A8 GEMM TOPS + % INT8 MFMA peak (prefill); decode GB/s as % of HBM peak"
 
@@ -324,6 +325,26 @@ def extras(torch, L, _sp, T, chk):
                                 "TOPS": round(2.0 * M * N * K / us_w / 1e6, 1)}
     del wqs
 
+    # The same prefill GEMM on the e4m3 path (finite codes: NaN codes never
+    # occur in quantized data).
+    def F8(*shape):
+        mag = torch.randint(0, 0x7F, shape, dtype=torch.int32, generator=g, device=dev)
+        sgn = torch.randint(0, 2, shape, dtype=torch.int32, generator=g, device=dev) << 7
+        return (mag | sgn).to(torch.uint8)
+    wqs = [F8(N, K) for _ in range(3)]
+    xq8 = F8(M, K)
+    fns = [lambda w=w: chk(L.sq_gemm_fp8_dequant(P(xq8), P(w), M, N, K, P(xs), 1, P(ws), P(y),
+                                                 2, sp), "gemm fp8") for w in wqs]
+    us = _time_loop(torch, fns, 30)
+    tf = 2.0 * M * N * K / us / 1e6
+    res["fp8_gemm_prefill_cold"] = {"us": round(us, 2), "TFLOPS": round(tf, 1),
+                                    "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                                    "frac_attainable": round(tf / attainable, 4)}
+    us_w = _time_loop(torch, fns[:1], 30)
+    res["fp8_gemm_prefill_warm"] = {"us": round(us_w, 2),
+                                    "TFLOPS": round(2.0 * M * N * K / us_w / 1e6, 1)}
+    del wqs
+
     # Decode: M in {1, 8, 32}, K = 8192, N = 28672, 3 rotating weight copies.
     M, N, K = 32, 28672, 8192
     wqs = [R(N, K) for _ in range(3)]
@@ -340,6 +361,19 @@ def extras(torch, L, _sp, T, chk):
                         "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
     res["decode"] = dec
     del wqs
+    wqs = [F8(N, K) for _ in range(3)]
+    dec = {}
+    for m in (1, 8, 32):
+        xq, xs = F8(m, K), U(m, 1e-2)
+        y = torch.empty((m, N), dtype=torch.float16, device=dev)
+        fns = [lambda w=w, xq=xq, xs=xs, y=y, m=m: chk(L.sq_gemm_fp8_dequant(
+            P(xq), P(w), m, N, K, P(xs), 1, P(ws), P(y), 1, sp), "decode fp8") for w in wqs]
+        us = _time_loop(torch, fns, 30)
+        b = N * K + m * K + m * N * 2 + 4 * m + 4 * N
+        dec[f"M{m}"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                        "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    res["fp8_decode"] = dec
+    del wqs
 
     # Activation quantization and abs-max on a 940 MB stream (X fp16 [65536, 7168]).
     M, K = 65536, 7168
@@ -354,6 +388,10 @@ def extras(torch, L, _sp, T, chk):
     b = M * K * 3 + 4 * K + 4 * M
     res["quantize_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
                               "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+    us = _time_loop(torch, [lambda: chk(L.sq_quantize_act_fp8(
+        P(Xs), 1, M, K, P(inv), 1, None, P(xq), P(xs), sp), "quant fp8")], 10)
+    res["fp8_quantize_stream"] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                                  "frac_hbm": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
     us = _time_loop(torch, [lambda: chk(L.sq_absmax_reduce(P(Xs), 1, M, K, 0, P(am), sp),
                                         "absmax")], 10)
     b = M * K * 2 + 4 * K
@@ -428,6 +466,23 @@ def extras(torch, L, _sp, T, chk):
         "per_gemm": per, "total_us": round(total_us, 2),
         "TOPS": round(total_ops / total_us / 1e6, 1),
         "frac_int8_peak": round(total_ops / total_us / 1e6 / PEAK_INT8_TOPS, 4)}
+    # ... and on the e4m3 path.
+    total_us, total_ops, per = 0.0, 0.0, {}
+    for gname, members in groups:
+        n = sum(dims[m][0] for m in members)
+        k = dims[members[0]][1]
+        xq, wq, xs, ws = F8(M, k), F8(n, k), U(M, 1e-2), U(n, 1e-3)
+        y = torch.empty((M, n), dtype=torch.float16, device=dev)
+        us = _time_loop(torch, [lambda: chk(L.sq_gemm_fp8_dequant(
+            P(xq), P(wq), M, n, k, P(xs), 1, P(ws), P(y), 1, sp), "dec1024 fp8")], 50)
+        ops = 2.0 * M * n * k
+        per[gname] = {"N": n, "K": k, "us": round(us, 2), "TFLOPS": round(ops / us / 1e6, 1)}
+        total_us += us
+        total_ops += ops
+    res["fp8_decoder_1024_batched"] = {
+        "per_gemm": per, "total_us": round(total_us, 2),
+        "TFLOPS": round(total_ops / total_us / 1e6, 1),
+        "frac_fp8_peak": round(total_ops / total_us / 1e6 / PEAK_FP8_TFLOPS, 4)}
     return res
 
 

@@ -167,6 +167,25 @@ def test_gemm_fp8_parity(torch, M, N, K, ydt, per_row, tile):
     print(f"\ngemm_fp8 M={M} N={N} K={K}: worst error / bound {worst:.3f}")
 
 
+# Decode kernel (M <= 32): every rows-per-block choice, K not a multiple of
+# the 4-wave split, ragged N.
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1000, 1024), (5, 256, 384), (8, 4096, 8192), (12, 520, 1024), (16, 1024, 256),
+    (20, 777, 2048), (24, 512, 128), (32, 3000, 4096)])
+def test_gemm_fp8_decode_parity(torch, M, N, K):
+    xq = _codes(M * 11 + K, (M, K), 2.0)
+    wq = _codes(N * 13 + K, (N, K), 0.5)
+    rng = np.random.default_rng(M * N + K)
+    xs = (rng.random(M) * 0.02 + 1e-3).astype(np.float32)
+    ws = (rng.random(N) * 0.002 + 1e-5).astype(np.float32)
+    log(f"gemm_fp8 decode M={M} N={N} K={K}")
+    y = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                            out_dtype=torch.float32)
+    _, acc, ab, bs = oracle.gemm_fp8_dequant(xq, wq, xs, ws, per_row=1)
+    worst = _check_gemm(host(y, torch), "f32", xs, ws, acc, ab, bs, True, K)
+    print(f"\ngemm_fp8 decode M={M} N={N} K={K}: worst error / bound {worst:.3f}")
+
+
 def test_fp8_layer_prefill_full_size(torch):
     """The prefill layer (X fp16 [256,7168], W fp16 [28672,7168], alpha 0.5,
     per-token) through the e4m3 path: codes and steps bit-exact at full size,

@@ -34,6 +34,7 @@
 namespace sq {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int int8x __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -835,6 +836,10 @@ gemm_pp(GemmArgs p) {
 //
 // K order inside the MFMA is free for integer sums: both operands use
 // "lane group g of step s holds bytes 64 s + 16 g .. + 15 of the stage".
+// The e4m3 form (F8, U = 2) feeds one v_mfma_f32_16x16x128_f8f6f4 per stage
+// with each lane's chunks of both steps as one 32-byte operand, built the
+// same way for weights and tokens, and sums the waves' fp32 partials in a
+// fixed order.
 template <int U>
 __device__ __forceinline__ int dec_swz(int r) {
     return (r / (4 / U)) & (4 * U - 1);
@@ -852,9 +857,10 @@ __device__ __forceinline__ void wait_stages(int later) {
     }
 }
 
-template <int NF, int FT, int U, int S, int YDT, bool NT>
+template <int NF, int FT, int U, int S, int YDT, bool NT, bool F8 = false>
 __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
     static_assert(U == 1 || U == 2 || U == 4, "stage width");
+    static_assert(!F8 || U == 2, "e4m3: two 64-byte steps per MFMA");
     static_assert(S >= 2 && S <= 6, "ring depth");
     constexpr int NR = 16 * NF;
     constexpr int NFR = NF + FT;                 // fragments per stage
@@ -931,11 +937,14 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
         }
     };
 
-    int4v acc[NF][FT];
+    using DAcc = std::conditional_t<F8, f32x4, int4v>;
+    DAcc acc[NF][FT];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int t = 0; t < FT; ++t) acc[f][t] = int4v{0, 0, 0, 0};
+        for (int t = 0; t < FT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[f][t][v] = 0;
 
     // Reader side: lane (g = lane / 16, i = lane % 16) takes row i, chunk
     // 4 s + g of step s.
@@ -957,6 +966,33 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
         }
         const char *sb = smem_w + (t % S) * SLOT;
         const int off = (s0 + t) * 64 * U;
+        if constexpr (F8) {
+            int4v a[2][NF], b[2][FT];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int c = 4 * st + rg;
+                const bool ok = off + 16 * c < K;
+                const int pos = 16 * (c ^ fi);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                    const int4v v = *reinterpret_cast<const int4v *>(sb + f * U * 1024 + pos);
+                    a[st][f] = ok ? v : int4v{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int x = 0; x < FT; ++x)
+                    b[st][x] = *reinterpret_cast<const int4v *>(sb + (NF + x) * U * 1024 + pos);
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int x = 0; x < FT; ++x) {
+                    const int8x av = __builtin_shufflevector(a[0][f], a[1][f], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const int8x bv = __builtin_shufflevector(b[0][x], b[1][x], 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[f][x] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc[f][x], 0, 0, 0, 0, 0, 0);
+                }
+            continue;
+        }
 #pragma unroll
         for (int st = 0; st < U; ++st) {
             const int c = 4 * st + rg;
@@ -981,7 +1017,8 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with its ring: reuse it for the sums
 
-    int *red = reinterpret_cast<int *>(smem);  // [wave][f][t][v * 64 + lane]
+    using RedT = std::conditional_t<F8, float, int>;
+    RedT *red = reinterpret_cast<RedT *>(smem);  // [wave][f][t][v * 64 + lane]
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -1002,13 +1039,13 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
         if (m >= M || nn >= N) continue;
         const int f = nl >> 4, i = nl & 15, t = ml >> 4, j = ml & 15;
         const int l = (i >> 2) * 16 + j, v = i & 3;
-        int a = 0;
+        RedT a = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) a += red[((w * NF + f) * FT + t) * 256 + v * 64 + l];
         const float cs = x_own[q] * w_own;
         const int64_t o = (int64_t)m * N + nn;
         store_y<YDT>(p.y, o, (float)a * cs);
-        if (p.acc_out) p.acc_out[o] = a;
+        if constexpr (!F8) if (p.acc_out) p.acc_out[o] = a;
     }
 }
 
@@ -1034,12 +1071,12 @@ static void launch_pipe_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     else gemm_pp<BM, BN, WM, WN, STA, STB, BF16, SIDE, F8><<<grid, block, 0, stream>>>(a);
 }
 
-template <int NF, int FT, int U, int S, bool NT>
+template <int NF, int FT, int U, int S, bool NT, bool F8 = false>
 static void launch_dec_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     dim3 grid((unsigned)((a.N + 16 * NF - 1) / (16 * NF))), block(256);
-    if (y_dt == F32) gemm_dec<NF, FT, U, S, F32, NT><<<grid, block, 0, stream>>>(a);
-    else if (y_dt == F16) gemm_dec<NF, FT, U, S, F16, NT><<<grid, block, 0, stream>>>(a);
-    else gemm_dec<NF, FT, U, S, BF16, NT><<<grid, block, 0, stream>>>(a);
+    if (y_dt == F32) gemm_dec<NF, FT, U, S, F32, NT, F8><<<grid, block, 0, stream>>>(a);
+    else if (y_dt == F16) gemm_dec<NF, FT, U, S, F16, NT, F8><<<grid, block, 0, stream>>>(a);
+    else gemm_dec<NF, FT, U, S, BF16, NT, F8><<<grid, block, 0, stream>>>(a);
 }
 
 // Tile shape: the candidate whose tiles fill the 256 CUs best, weighted by
@@ -1105,9 +1142,9 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     }
 }
 
-// e4m3 x e4m3 -> fp32 GEMM with the same dequant epilogue (K % 128 == 0).
-// Every M uses the pipelined kernel (for M <= 32 the 128 x 128 tile, its
-// rows past M clamped to the last one).
+// e4m3 x e4m3 -> fp32 GEMM with the same dequant epilogue (K % 128 == 0):
+// the decode kernel for M <= 32 (same ring shapes as int8), else the
+// pipelined one.
 void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
                      const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
                      hipStream_t stream) {
@@ -1117,7 +1154,14 @@ void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
     a.wq = reinterpret_cast<const int8_t *>(wq);
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.xs = x_scale; a.xs_per_row = per_row; a.ws = w_scale; a.y = y;
-    int tile = M <= 32 ? 2 : pick_tile(M, N);
+    if (M <= 32) {
+        if (M <= 8) launch_dec_t<1, 1, 2, 4, true, true>(a, y_dt, stream);
+        else if (M <= 16) launch_dec_t<4, 1, 2, 2, true, true>(a, y_dt, stream);
+        else if (M <= 24) launch_dec_t<2, 2, 2, 2, true, true>(a, y_dt, stream);
+        else launch_dec_t<4, 2, 2, 2, true, true>(a, y_dt, stream);
+        return;
+    }
+    int tile = pick_tile(M, N);
     if (const char *e = getenv("SQ_GEMM_TILE")) {
         if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
     }
