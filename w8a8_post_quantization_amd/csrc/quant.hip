@@ -89,11 +89,31 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
+// Four values -> four int8 codes: clamp(round_half_even(fl(v * inv)), +-127).
+// Adding 1.5 2^23 to a value below 2^22 in magnitude rounds it to an integer,
+// half to even, and leaves that integer's two's complement low byte in the
+// low byte of the sum's bits; v_perm gathers the four low bytes.  With a
+// per-row step (CLAMP = false) |fl(v * fl(127 / a))| <= 127 (1 + 2^-24)^2
+// because |v| <= a, so the clamp cannot act; with a fixed step it clamps
+// first (rounding and clamping commute at integer bounds).
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d, float inv) {
+    float z[4] = {a * inv, b * inv, c * inv, d * inv};
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (CLAMP) z[i] = __builtin_amdgcn_fmed3f(z[i], -127.0f, 127.0f);
+        u[i] = __float_as_uint(z[i] + 12582912.0f);
+    }
+    return __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u),
+                                 __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u), 0x05040100u);
+}
+
 template <bool FP8> struct QMax;
 template <> struct QMax<false> { static constexpr float v = 127.0f; };
 template <> struct QMax<true> { static constexpr float v = 448.0f; };
 
-template <int DT, bool FP8 = false>
+template <int DT, bool FP8, bool CLAMP>
 __device__ __forceinline__ void store_q(int8_t *__restrict__ q, int64_t e0, const float *v,
                                         float inv) {
     if constexpr (FP8) {
@@ -107,15 +127,11 @@ __device__ __forceinline__ void store_q(int8_t *__restrict__ q, int64_t e0, cons
         }
     } else if constexpr (Vec<DT>::n == 8) {
         uint2 o;
-        o.x = pack4(quant_i8(v[0], inv), quant_i8(v[1], inv), quant_i8(v[2], inv),
-                    quant_i8(v[3], inv));
-        o.y = pack4(quant_i8(v[4], inv), quant_i8(v[5], inv), quant_i8(v[6], inv),
-                    quant_i8(v[7], inv));
+        o.x = pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv);
+        o.y = pack_i8x4<CLAMP>(v[4], v[5], v[6], v[7], inv);
         *reinterpret_cast<uint2 *>(q + e0) = o;
     } else {
-        *reinterpret_cast<uint32_t *>(q + e0) =
-            pack4(quant_i8(v[0], inv), quant_i8(v[1], inv), quant_i8(v[2], inv),
-                  quant_i8(v[3], inv));
+        *reinterpret_cast<uint32_t *>(q + e0) = pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv);
     }
 }
 
@@ -199,7 +215,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 if (vi < nvec) {
                     float v[V];
                     scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm);
-                    store_q<DT, FP8>(qr, vi * V, v, inv);
+                    store_q<DT, FP8, false>(qr, vi * V, v, inv);
                 }
             }
         };
@@ -244,13 +260,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
-                store_q<DT, FP8>(qr, vi * V, v, inv);
+                store_q<DT, FP8, false>(qr, vi * V, v, inv);
             }
         } else {
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
-                store_q<DT, FP8>(qr, vi * V, v, inv_static);
+                store_q<DT, FP8, true>(qr, vi * V, v, inv_static);
             }
         }
     }
@@ -326,7 +342,7 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
 #pragma unroll
                 for (int i = 0; i < V; ++i) v[i] = v[i] * m[it][i];
             }
-            store_q<DT, FP8>(qr, vi * V, v, inv);
+            store_q<DT, FP8, !DYN>(qr, vi * V, v, inv);
         }
     }
 }

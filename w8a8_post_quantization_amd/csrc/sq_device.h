@@ -58,18 +58,6 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Round half to even (v_rndne_f32), clamp to [-127, 127], as int.
-__device__ __forceinline__ int quant_i8(float v, float inv) {
-    float r = __builtin_rintf(v * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
-
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-           ((uint32_t)(d & 0xff) << 24);
-}
-
 // Narrow fp32 to the output type with round-to-nearest-even.
 template <int DT> struct OutT;
 template <> struct OutT<F32> { using T = float; };
