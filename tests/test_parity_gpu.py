@@ -138,7 +138,7 @@ GEMM_CASES = [
     (513, 257, 1040, "f16", 1, "0"), (70, 300, 128, "bf16", 1, "1"), (96, 96, 64, "f32", 1, "0"),
     (2048, 512, 4096, "f16", 1, None), (300, 300, 128, "f16", 1, "0"), (129, 260, 256, "f32", 1, "2"),
     (264, 136, 384, "bf16", 1, "1"),
-    # decode path (M <= 32): every rows-per-block choice (M <= 8, 16, 24, 32),
+    # decode path (M <= 32): every rows-per-block choice (M <= 8, 16, 32),
     # K below one 128-byte stage, K not a multiple of the stage, ragged N
     (1, 1000, 8192, "f16", 1, None), (8, 333, 512, "f32", 1, None),
     (16, 64, 1024, "f32", 0, None), (17, 100, 256, "bf16", 1, None),
