@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (3 launches): the "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--profile-gemms", action="store_true",
+                    help="only run the GEMM workloads eagerly, a few launches each, for "
+                         "rocprofv3 counter runs (MFMA utilisation, HBM bytes)")
     return ap.parse_args()
 
 
@@ -126,10 +129,60 @@ class Timer:
         return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / len(ps)
 
 
+def profile_gemms():
+    """Each GEMM workload launched eagerly (no graph), 3 times, so that a
+    counter run sees one dispatch per launch: the prefill shape in int8 and
+    e4m3 (3 rotating weight copies, beyond the last-level cache), the batched
+    q|k|v GEMM of the hidden-1024 layer, and decode at M = 1, 8, 32."""
+    import torch
+
+    import w8a8_post_quantization_amd as sq
+
+    L = sq.lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: t.data_ptr()  # noqa: E731
+    R = lambda *shape: torch.randint(-127, 128, shape, dtype=torch.int8, generator=g,  # noqa: E731
+                                     device=dev)
+    U = lambda n, scale: torch.rand(n, generator=g, device=dev) * scale + scale * 0.1  # noqa: E731
+
+    def F8(*shape):
+        mag = torch.randint(0, 0x7F, shape, dtype=torch.int32, generator=g, device=dev)
+        sgn = torch.randint(0, 2, shape, dtype=torch.int32, generator=g, device=dev) << 7
+        return (mag | sgn).to(torch.uint8)
+
+    def chk(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {L.sq_status_str(rc).decode()}")
+
+    ran = []
+    for name, M, N, K, ydt in (("prefill_30b", 256, 28672, 7168, 2), ("qkv_1024", 4096, 4096, 1024, 1),
+                               ("decode_M1", 1, 28672, 8192, 1), ("decode_M8", 8, 28672, 8192, 1),
+                               ("decode_M32", 32, 28672, 8192, 1)):
+        for kind, gen, fn in (("i8", R, L.sq_gemm_i8_dequant), ("f8", F8, L.sq_gemm_fp8_dequant)):
+            ws_ = [gen(N, K) for _ in range(3)]
+            x = gen(M, K)
+            xs, ws = U(M, 1e-2), U(N, 1e-3)
+            y = torch.empty((M, N), dtype=torch.bfloat16 if ydt == 2 else torch.float16, device=dev)
+            for w in ws_:
+                if kind == "i8":
+                    chk(fn(P(x), P(w), M, N, K, P(xs), 1, P(ws), P(y), ydt, None, sp), name)
+                else:
+                    chk(fn(P(x), P(w), M, N, K, P(xs), 1, P(ws), P(y), ydt, sp), name)
+            torch.cuda.synchronize()
+            ran.append(f"{name}_{kind}")
+            del ws_
+    print(json.dumps({"profile_gemms": ran}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.profile_gemms:
+        profile_gemms()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
