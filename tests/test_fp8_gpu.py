@@ -171,7 +171,8 @@ def test_gemm_fp8_parity(torch, M, N, K, ydt, per_row, tile):
 # the 4-wave split, ragged N.
 @pytest.mark.parametrize("M,N,K", [
     (1, 1000, 1024), (5, 256, 384), (8, 4096, 8192), (12, 520, 1024), (16, 1024, 256),
-    (20, 777, 2048), (24, 512, 128), (32, 3000, 4096)])
+    (20, 777, 2048), (24, 512, 128), (32, 3000, 4096),
+    (32, 11200, 256), (20, 11163, 1024)])   # 112-row blocks, ragged last block
 def test_gemm_fp8_decode_parity(torch, M, N, K):
     xq = _codes(M * 11 + K, (M, K), 2.0)
     wq = _codes(N * 13 + K, (N, K), 0.5)

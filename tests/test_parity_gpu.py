@@ -146,6 +146,10 @@ GEMM_CASES = [
     (3, 50, 16, "f16", 1, None), (12, 130, 208, "bf16", 1, None),
     (24, 97, 1040, "f32", 1, None), (25, 300, 4112, "f16", 1, None),
     (2, 4100, 1024, "bf16", 0, None), (9, 63, 48, "f16", 1, None),
+    # 17..32 tokens with N wide enough that 112-row blocks fill the CUs
+    # better than 128-row ones (the 7-fragment block; ragged last block)
+    (32, 11200, 256, "bf16", 1, None), (20, 11163, 1040, "f16", 1, None),
+    (17, 11200, 16, "f32", 0, None),
 ]
 YDT = {"f32": 0, "f16": 1, "bf16": 2}
 

@@ -861,7 +861,7 @@ template <int NF, int FT, int U, int S, int YDT, bool NT, bool F8 = false>
 __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
     static_assert(U == 1 || U == 2 || U == 4, "stage width");
     static_assert(!F8 || U == 2, "e4m3: two 64-byte steps per MFMA");
-    static_assert(256 % (16 * NF) == 0, "the epilogue maps threads to rows with 256 / (16 NF)");
+    static_assert((16 * NF * 16 * FT) % 256 == 0, "whole outputs per thread");
     static_assert(S >= 2 && S <= 6, "ring depth");
     constexpr int NR = 16 * NF;
     constexpr int NFR = NF + FT;                 // fragments per stage
@@ -902,15 +902,18 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
         }
     }
 
-    // Steps of this thread's outputs, fetched before the loop so the epilogue
-    // issues stores only (and so they are older than every ring load).
+    // Steps of this thread's outputs e = tid + 256 q (n fastest), fetched
+    // before the loop so the epilogue issues stores only (and so they are
+    // older than every ring load).  When NR divides 256 every output of a
+    // thread has the same weight row.
     constexpr int EPT = NR * 16 * FT / 256;
-    const int n_own = n0 + (tid % NR);
-    const float w_own = p.ws[n_own < N ? n_own : N - 1];
-    float x_own[EPT];
+    constexpr bool ONE_W = 256 % NR == 0;
+    float w_own[ONE_W ? 1 : EPT], x_own[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-        const int m = tid / NR + (256 / NR) * q;
+        const int e = tid + 256 * q;
+        const int nn = n0 + e % NR, m = e / NR;
+        if (!ONE_W || q == 0) w_own[ONE_W ? 0 : q] = p.ws[nn < N ? nn : N - 1];
         x_own[q] = p.xs[p.xs_per_row ? (m < M ? m : M - 1) : 0];
     }
 
@@ -1043,7 +1046,7 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
         RedT a = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) a += red[((w * NF + f) * FT + t) * 256 + v * 64 + l];
-        const float cs = x_own[q] * w_own;
+        const float cs = x_own[q] * w_own[ONE_W ? 0 : q];
         const int64_t o = (int64_t)m * N + nn;
         store_y<YDT>(p.y, o, (float)a * cs);
         if constexpr (!F8) if (p.acc_out) p.acc_out[o] = a;
@@ -1078,6 +1081,16 @@ static void launch_dec_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     if (y_dt == F32) gemm_dec<NF, FT, U, S, F32, NT, F8><<<grid, block, 0, stream>>>(a);
     else if (y_dt == F16) gemm_dec<NF, FT, U, S, F16, NT, F8><<<grid, block, 0, stream>>>(a);
     else gemm_dec<NF, FT, U, S, BF16, NT, F8><<<grid, block, 0, stream>>>(a);
+}
+
+// Decode above 16 tokens: 112 weight rows per block instead of 128 when
+// that fills the 256 CUs clearly better (N = 28672: 256 blocks against 224).
+static bool dec_rows_112(int64_t N) {
+    auto fill = [](int64_t blocks) {  // busy fraction of the CUs over all rounds
+        const int64_t rounds = (blocks + 255) / 256;
+        return (double)blocks / (double)(rounds * 256);
+    };
+    return fill((N + 111) / 112) > fill((N + 127) / 128) + 0.02;
 }
 
 // Tile shape: the candidate whose tiles fill the 256 CUs best, weighted by
@@ -1120,6 +1133,7 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         // weight stream then fetches each line once).
         if (M <= 8) launch_dec_t<1, 1, 2, 4, true>(a, y_dt, stream);
         else if (M <= 16) launch_dec_t<4, 1, 2, 2, true>(a, y_dt, stream);
+        else if (dec_rows_112(N)) launch_dec_t<7, 2, 2, 2, true>(a, y_dt, stream);
         else launch_dec_t<8, 2, 2, 2, true>(a, y_dt, stream);
         return;
     }
@@ -1158,6 +1172,7 @@ void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
     if (M <= 32) {
         if (M <= 8) launch_dec_t<1, 1, 2, 4, true, true>(a, y_dt, stream);
         else if (M <= 16) launch_dec_t<4, 1, 2, 2, true, true>(a, y_dt, stream);
+        else if (dec_rows_112(N)) launch_dec_t<7, 2, 2, 2, true, true>(a, y_dt, stream);
         else launch_dec_t<8, 2, 2, 2, true, true>(a, y_dt, stream);
         return;
     }
