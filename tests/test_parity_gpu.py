@@ -197,18 +197,29 @@ def test_gemm_extremal_values(torch):
 
 # ---------------------------------------------------------------- a6
 
-@pytest.mark.parametrize("M,N,K,thr", [(300, 200, 512, 6.0), (64, 130, 256, float("inf")),
-                                       (40, 96, 128, 0.5), (2048, 256, 4096, 6.0)])
-def test_mixed_parity(torch, M, N, K, thr):
+# The side-term GEMM: 256 x 128 tiles (ragged M and N), 128 x 128 tiles when
+# forced, the non-pipelined tile when K % 128 != 0, more than 32 outlier
+# columns (threshold 0.5: the side operands are staged 32 columns at a time).
+@pytest.mark.parametrize("M,N,K,thr,tile", [
+    (300, 200, 512, 6.0, None), (64, 130, 256, float("inf"), None), (40, 96, 128, 0.5, None),
+    (2048, 256, 4096, 6.0, None), (300, 200, 512, 6.0, "2"), (100, 150, 208, 6.0, None),
+    (260, 300, 384, 0.5, None)])
+def test_mixed_parity(torch, M, N, K, thr, tile):
     import synth
 
     cfg = synth.llm_int8_2048(M=M, N=N, K=K)
     X, W = cfg["X"], cfg["W"]
     wq_o, ws_o = oracle.smooth_weights(W, None)
-    log(f"mixed M={M} N={N} K={K} thr={thr}")
+    log(f"mixed M={M} N={N} K={K} thr={thr} tile={tile}")
     wq, ws = sq.smooth_weights(dev(W, torch))
     assert_bits_equal(host(wq, torch), wq_o, "wq")
-    y, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), thr, with_count=True)
+    if tile is not None:
+        os.environ["SQ_GEMM_TILE"] = tile
+    try:
+        y, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), thr,
+                                      with_count=True)
+    finally:
+        os.environ.pop("SQ_GEMM_TILE", None)
     r = oracle.int8_mixed_matmul(X, wq_o, ws_o, W, thr)
     assert int(host(cnt, torch)[0]) == r["idx"].size
     assert_bits_equal(host(y, torch), r["y"], "y")

@@ -594,10 +594,11 @@ __device__ __forceinline__ void sched_tail() {
 // registers: a quarter's LDS reads overlap the previous quarter's MFMAs, and
 // after the stage barrier the next stage's first reads overlap the last
 // quarter's MFMAs.  Weight rows are the MFMA A operand (see epilogue_nt).
-// The side-term variant asks for two waves per SIMD: its 128x128 tiles are
-// small, and one wave per SIMD halves how many tiles a CU has in flight.
+// The four-wave 128x128 side-term variant asks for two blocks per CU: its
+// tiles are small, and one wave per SIMD halves how many tiles a CU has in
+// flight.  The eight-wave 256x128 side-term tile runs one block per CU.
 template <int BM, int BN, int WM, int WN, int STA, int STB, int YDT, bool SIDE, bool F8 = false>
-__global__ __launch_bounds__(64 * WM * WN, SIDE ? 2 : 1) __attribute__((amdgpu_waves_per_eu(SIDE ? 2 : 1, 4))) void
+__global__ __launch_bounds__(64 * WM * WN, (SIDE && WM * WN == 4) ? 2 : 1) __attribute__((amdgpu_waves_per_eu(SIDE ? 2 : 1, 4))) void
 gemm_pp(GemmArgs p) {
     constexpr int BK = 128;
     constexpr int NW = WM * WN;  // waves
@@ -1118,9 +1119,17 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     a.xq = xq; a.wq = wq; a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.xs = x_scale; a.xs_per_row = per_row; a.ws = w_scale; a.y = y; a.acc_out = acc_out;
     const bool pipe = K % 128 == 0;
+    // SQ_GEMM_TILE=0|1|2 forces a tile shape (for coverage of every shape).
+    int tile = pick_tile(M, N);
+    if (const char *e = getenv("SQ_GEMM_TILE")) {
+        if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
+    }
     if (side) {
+        // With the side term 256 x 256 tiles would need the side sums next
+        // to 128 accumulator registers: the 256-row choices take 256 x 128.
         a.x16 = side->x16; a.w16 = side->w16; a.idx = side->idx; a.count = side->count;
-        if (pipe) launch_pipe_t<128, 128, 2, 2, 2, 2, true>(a, y_dt, stream);
+        if (pipe && tile < 2) launch_pipe_t<256, 128, 4, 2, 3, 3, true>(a, y_dt, stream);
+        else if (pipe) launch_pipe_t<128, 128, 2, 2, 2, 2, true>(a, y_dt, stream);
         else launch_tile_t<128, 128, 2, 2, true>(a, y_dt, stream);
         return;
     }
@@ -1128,7 +1137,8 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         // Weight rows per block and ring shape by token count: more rows
         // per block as M grows (each block re-reads all M token rows: 128
         // weight rows per block above 16 tokens, measured 43 us against
-        // 47 us with 64 at M = 32), two 64-byte K steps a stage so that a
+        // 47 us with 64 at M = 32, or 112 where that fills the CUs better:
+        // 40 us at N = 28672), two 64-byte K steps a stage so that a
         // stage covers whole 128-byte lines of every row (the nontemporal
         // weight stream then fetches each line once).
         if (M <= 8) launch_dec_t<1, 1, 2, 4, true>(a, y_dt, stream);
@@ -1136,11 +1146,6 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         else if (dec_rows_112(N)) launch_dec_t<7, 2, 2, 2, true>(a, y_dt, stream);
         else launch_dec_t<8, 2, 2, 2, true>(a, y_dt, stream);
         return;
-    }
-    // SQ_GEMM_TILE=0|1|2 forces a tile shape (for coverage of every shape).
-    int tile = pick_tile(M, N);
-    if (const char *e = getenv("SQ_GEMM_TILE")) {
-        if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
     }
     if (pipe) {
         switch (tile) {

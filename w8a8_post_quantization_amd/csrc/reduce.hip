@@ -179,7 +179,8 @@ __global__ __launch_bounds__(1024) void outlier_list_kernel(const float *__restr
                                                             int64_t K, float threshold,
                                                             float *__restrict__ mask,
                                                             int32_t *__restrict__ idx,
-                                                            int32_t *__restrict__ count) {
+                                                            int32_t *__restrict__ count,
+                                                            int32_t *__restrict__ count_out) {
     __shared__ int wave_cnt[16];
     __shared__ int base_s;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -206,24 +207,24 @@ __global__ __launch_bounds__(1024) void outlier_list_kernel(const float *__restr
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) *count = base_s;
+    if (threadIdx.x == 0) {
+        *count = base_s;
+        if (count_out) *count_out = base_s;
+    }
 }
 
-__global__ void copy_i32_kernel(const int32_t *src, int32_t *dst) { *dst = *src; }
 __global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
 
-void launch_copy_i32(const int32_t *src, int32_t *dst, hipStream_t stream) {
-    copy_i32_kernel<<<dim3(1), dim3(1), 0, stream>>>(src, dst);
-}
 void launch_copy_f32(const float *src, float *dst, hipStream_t stream) {
     copy_f32_kernel<<<dim3(1), dim3(1), 0, stream>>>(src, dst);
 }
 
 void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
-                         float *mask, int32_t *idx, int32_t *count, hipStream_t stream) {
+                         float *mask, int32_t *idx, int32_t *count, int32_t *count_out,
+                         hipStream_t stream) {
     launch_absmax(x, F16, M, K, 0, colmax, stream);
     outlier_list_kernel<<<dim3(1), dim3(1024), 0, stream>>>(colmax, K, threshold, mask, idx,
-                                                            count);
+                                                            count, count_out);
 }
 
 }  // namespace sq

@@ -270,12 +270,11 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
     auto *idx = reinterpret_cast<int32_t *>(ws + L.idx);
     auto *count = reinterpret_cast<int32_t *>(ws + L.count);
     hipStream_t s = st(stream);
-    sq::launch_outlier_prep(x, M, K, threshold, colmax, mask, idx, count, s);
+    sq::launch_outlier_prep(x, M, K, threshold, colmax, mask, idx, count, n_outliers_out, s);
     sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
     sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
                       count};
     sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, nullptr, &side, s);
-    if (n_outliers_out) sq::launch_copy_i32(count, n_outliers_out, s);
     return finish();
 }
 

@@ -47,9 +47,11 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
                  int32_t *acc_out, const SideTerm *side, hipStream_t stream);
 
 // LLM.int8() preparation: column abs-max of x into colmax, then the mask
-// (1.0 keep / 0.0 outlier), the ascending O list and its count.
+// (1.0 keep / 0.0 outlier), the ascending O list and its count (also into
+// count_out when that is not null).
 void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
-                         float *mask, int32_t *idx, int32_t *count, hipStream_t stream);
+                         float *mask, int32_t *idx, int32_t *count, int32_t *count_out,
+                         hipStream_t stream);
 
 // Folding 1/s into the norm's parameters, and the fused fp16 norm ->
 // int8 row quantizer (K <= 16384).
@@ -61,7 +63,6 @@ void launch_norm_quant(const void *x, int64_t M, int64_t K, int norm, const floa
 
 // Tiny device-to-device copies done by a kernel (no copy-engine or memset
 // nodes, so the calls stay capturable in a HIP graph).
-void launch_copy_i32(const int32_t *src, int32_t *dst, hipStream_t stream);
 void launch_copy_f32(const float *src, float *dst, hipStream_t stream);
 
 }  // namespace sq
