@@ -136,7 +136,8 @@ def profile_gemms():
     """Each GEMM workload launched eagerly (no graph), 3 times, so that a
     counter run sees one dispatch per launch: the prefill shape in int8 and
     e4m3 (3 rotating weight copies, beyond the last-level cache), the batched
-    q|k|v GEMM of the hidden-1024 layer, and decode at M = 1, 8, 32."""
+    q|k|v GEMM of the hidden-1024 layer, decode at M = 1, 8, 32, and the
+    LLM.int8() call on its 2048 x 4096 x 4096 workload."""
     import torch
 
     import w8a8_post_quantization_amd as sq
@@ -176,6 +177,24 @@ def profile_gemms():
             torch.cuda.synchronize()
             ran.append(f"{name}_{kind}")
             del ws_
+    # LLM.int8() on its workload (fp16 X with 6 outlier columns of ~20 in
+    # about half the rows): the side-term GEMM among its kernels.
+    M, N, K = 2048, 4096, 4096
+    x = torch.randn((M, K), generator=g, device=dev)
+    x[:, torch.randperm(K, generator=g, device=dev)[:6]] *= 20.0
+    x = x.half()
+    w16 = (torch.randn((N, K), generator=g, device=dev) * 0.02).half()
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    ws = torch.empty(N, dtype=torch.float32, device=dev)
+    chk(L.sq_smooth_weights(P(w16), 1, N, K, None, P(wq), P(ws), sp), "llm_int8 weights")
+    need = L.sq_int8_mixed_matmul_workspace(M, K)
+    work = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    for _ in range(3):
+        chk(L.sq_int8_mixed_matmul(P(x), M, K, P(wq), P(ws), P(w16), N, 6.0, P(work), need, P(y), 1,
+                                   None, sp), "llm_int8")
+    torch.cuda.synchronize()
+    ran.append("llm_int8")
     print(json.dumps({"profile_gemms": ran}), flush=True)
 
 
@@ -331,7 +350,10 @@ def _time_loop(torch, fns, iters):
     The calls are captured once into a HIP graph and the graph is replayed,
     so the figure is the kernels' own time, not the host's launch rate (the
     short kernels here take less time than a Python-level launch).  Each fn
-    launches on torch's current stream, which is the capture stream."""
+    launches on torch's current stream, which is the capture stream.  Five
+    untimed replays come first: on this GPU the first replays of a new
+    workload ran up to 25 % slower than its steady state (the cold prefill
+    GEMM: 83 us, then 73, then 66-68)."""
     for f in fns:
         f()
     torch.cuda.synchronize()
@@ -339,7 +361,8 @@ def _time_loop(torch, fns, iters):
     with torch.cuda.graph(g):
         for i in range(iters):
             fns[i % len(fns)]()
-    g.replay()
+    for _ in range(5):
+        g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 3
