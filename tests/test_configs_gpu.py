@@ -157,7 +157,8 @@ def test_llm_int8_2048(torch):
 
 def test_activation_stream(torch):
     """The 940 MB activation stream the benchmark times (X fp16
-    [65536,7168]): a1 and per-token a4 against the oracle."""
+    [65536,7168]): a1, and a4 per-token and static, int8 and e4m3, against
+    the oracle."""
     cfg = synth.stream_act()
     X = cfg["X"]
     inv = (1.0 / (oracle.absmax_cols(X[:1024]) + 1.0)).astype(np.float32)
@@ -166,3 +167,20 @@ def test_activation_stream(torch):
                       "amax")
     log("stream a4")
     _act(torch, X, inv)
+    # codes beyond the last-level cache size are stored nontemporally: the
+    # static int8 form and both e4m3 forms of that store path as well
+    log("stream a4 static")
+    st = oracle.static_scale(oracle.absmax_cols(X), inv, 127.0)
+    _act(torch, X, inv, sq.SQ_PER_TENSOR_STATIC, st)
+    log("stream a4 e4m3 per-token")
+    xq8, xs8 = sq.quantize_act_fp8(dev(X, torch), dev(inv, torch))
+    xq8_o, xs8_o = oracle.quantize_act_fp8(X, inv)
+    assert_bits_equal(host(xs8, torch), xs8_o, "x_scale e4m3")
+    assert_bits_equal(host(xq8, torch), xq8_o, "xq e4m3")
+    log("stream a4 e4m3 static")
+    st8 = oracle.static_scale(oracle.absmax_cols(X), inv, 448.0)
+    xq8, xs8 = sq.quantize_act_fp8(dev(X, torch), dev(inv, torch), sq.SQ_PER_TENSOR_STATIC,
+                                   dev(st8, torch))
+    xq8_o, xs8_o = oracle.quantize_act_fp8(X, inv, oracle.PER_TENSOR_STATIC, st8)
+    assert_bits_equal(host(xs8, torch), xs8_o, "x_scale e4m3 static")
+    assert_bits_equal(host(xq8, torch), xq8_o, "xq e4m3 static")

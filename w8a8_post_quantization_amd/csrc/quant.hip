@@ -113,25 +113,37 @@ template <bool FP8> struct QMax;
 template <> struct QMax<false> { static constexpr float v = 127.0f; };
 template <> struct QMax<true> { static constexpr float v = 448.0f; };
 
-template <int DT, bool FP8, bool CLAMP>
+// NT: nontemporal stores, for outputs larger than the last-level cache
+// (they are not read back before being evicted anyway, and streaming them
+// past the caches measured 6.1 TB/s against 5.4 for plain stores on a
+// 940 MB -> 470 MB stream; below the cache size plain stores are faster and
+// leave the codes cached for the GEMM that reads them next).
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ void st_codes(int8_t *p, uint32_t a, uint32_t b) {
+    if constexpr (NT) __builtin_nontemporal_store(u2v{a, b}, reinterpret_cast<u2v *>(p));
+    else *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+}
+template <bool NT>
+__device__ __forceinline__ void st_codes(int8_t *p, uint32_t a) {
+    if constexpr (NT) __builtin_nontemporal_store(a, reinterpret_cast<uint32_t *>(p));
+    else *reinterpret_cast<uint32_t *>(p) = a;
+}
+
+template <int DT, bool FP8, bool CLAMP, bool NT = false>
 __device__ __forceinline__ void store_q(int8_t *__restrict__ q, int64_t e0, const float *v,
                                         float inv) {
     if constexpr (FP8) {
-        if constexpr (Vec<DT>::n == 8) {
-            uint2 o;
-            o.x = pack_fp8x4(v[0], v[1], v[2], v[3], inv);
-            o.y = pack_fp8x4(v[4], v[5], v[6], v[7], inv);
-            *reinterpret_cast<uint2 *>(q + e0) = o;
-        } else {
-            *reinterpret_cast<uint32_t *>(q + e0) = pack_fp8x4(v[0], v[1], v[2], v[3], inv);
-        }
+        if constexpr (Vec<DT>::n == 8)
+            st_codes<NT>(q + e0, pack_fp8x4(v[0], v[1], v[2], v[3], inv),
+                         pack_fp8x4(v[4], v[5], v[6], v[7], inv));
+        else
+            st_codes<NT>(q + e0, pack_fp8x4(v[0], v[1], v[2], v[3], inv));
     } else if constexpr (Vec<DT>::n == 8) {
-        uint2 o;
-        o.x = pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv);
-        o.y = pack_i8x4<CLAMP>(v[4], v[5], v[6], v[7], inv);
-        *reinterpret_cast<uint2 *>(q + e0) = o;
+        st_codes<NT>(q + e0, pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv),
+                     pack_i8x4<CLAMP>(v[4], v[5], v[6], v[7], inv));
     } else {
-        *reinterpret_cast<uint32_t *>(q + e0) = pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv);
+        st_codes<NT>(q + e0, pack_i8x4<CLAMP>(v[0], v[1], v[2], v[3], inv));
     }
 }
 
@@ -147,7 +159,8 @@ constexpr int kMulLds = 16384;
 // branch makes the compiler wait for all earlier memory operations first,
 // which would serialize the row's loads.  ITS = 0: rows longer than
 // 16 x 64 vectors, streamed twice (the second pass hits L2).
-template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW, bool FP8>
+template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW, bool FP8,
+          bool NTS>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
                                                          const float *__restrict__ mul_g,
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 if (vi < nvec) {
                     float v[V];
                     scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm);
-                    store_q<DT, FP8, false>(qr, vi * V, v, inv);
+                    store_q<DT, FP8, false, NTS>(qr, vi * V, v, inv);
                 }
             }
         };
@@ -260,13 +273,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
-                store_q<DT, FP8, false>(qr, vi * V, v, inv);
+                store_q<DT, FP8, false, NTS>(qr, vi * V, v, inv);
             }
         } else {
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
                 scaled<DT, HAS_MUL, MUL_LDS>(xr[vi], mul, vi * V, v);
-                store_q<DT, FP8, true>(qr, vi * V, v, inv_static);
+                store_q<DT, FP8, true, NTS>(qr, vi * V, v, inv_static);
             }
         }
     }
@@ -379,11 +392,18 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     dim3 grid((unsigned)blocks), block(256);
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
-#define SQ_Q(ITS, LDS)                                                                     \
-    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8><<<grid, block, shmem, stream>>>( \
+    // Codes larger than the 256 MB last-level cache are stored nontemporally.
+    const bool nts = rows * K > (int64_t)256 << 20;
+#define SQ_Q(ITS, LDS, NT)                                                                      \
+    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8, NT><<<grid, block, shmem, stream>>>( \
         xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw)
-#define SQ_QL(ITS) \
-    do { if (mul_lds) SQ_Q(ITS, true); else SQ_Q(ITS, false); } while (0)
+#define SQ_QL(ITS)                                    \
+    do {                                              \
+        if (mul_lds && nts) SQ_Q(ITS, true, true);    \
+        else if (mul_lds) SQ_Q(ITS, true, false);     \
+        else if (nts) SQ_Q(ITS, false, true);         \
+        else SQ_Q(ITS, false, false);                 \
+    } while (0)
     switch (its) {
         case 2: SQ_QL(2); break;
         case 4: SQ_QL(4); break;
