@@ -381,19 +381,23 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
 #undef SQ_B
         return;
     }
+    // Codes larger than the 256 MB last-level cache are stored nontemporally.
+    const bool nts = rows * K > (int64_t)256 << 20;
     // Rows per wave: enough blocks to fill the chip (>= ~1024), more rows
-    // per block when there are plenty, so the multiplier is staged rarely.
+    // per block when there are plenty, so the multiplier is staged rarely:
+    // up to 8 with plain stores (a3's 28672 rows: 7, 106 us against 112 with
+    // 2), up to MAX_RPW_NT with nontemporal ones (the 65536-row stream:
+    // 2 rows, 240 us against 265 with 8).
+    constexpr int64_t MAX_RPW_NT = 2;
     int64_t rpw = rows / (4 * 1024);
     if (rpw < 1) rpw = 1;
-    if (rpw > 8) rpw = 8;
+    if (rpw > (nts ? MAX_RPW_NT : 8)) rpw = nts ? MAX_RPW_NT : 8;
     const int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
     const bool mul_lds = HAS_MUL && K <= kMulLds;
     const size_t shmem = mul_lds ? (size_t)K * sizeof(float) : 0;
     dim3 grid((unsigned)blocks), block(256);
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
-    // Codes larger than the 256 MB last-level cache are stored nontemporally.
-    const bool nts = rows * K > (int64_t)256 << 20;
 #define SQ_Q(ITS, LDS, NT)                                                                      \
     quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8, NT><<<grid, block, shmem, stream>>>( \
         xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw)
