@@ -374,6 +374,72 @@ def _time_loop(torch, fns, iters):
     return 1000.0 * a.elapsed_time(b) / (iters * reps)
 
 
+def measured_peaks(torch):
+    """What simple kernels get from this GPU (include/sq_peaks.h): the int8
+    and e4m3 matrix-core rate of an MFMA loop with no memory traffic, the
+    HBM rate of a 1 GiB read and of a 1 GiB -> 512 MiB 2:1 stream (the
+    quantizers' mix), and the shader clock sustained under each (clock
+    counter ticks over real-time counter ticks, times the real-time rate)."""
+    from w8a8_post_quantization_amd import build as hip_build
+
+    if not os.path.exists(hip_build.PEAKS_LIB_PATH):
+        raise RuntimeError(f"{hip_build.PEAKS_LIB_PATH} is missing: build first")
+    L = ctypes.CDLL(hip_build.PEAKS_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.sqp_mfma_loop.argtypes = [i32, i32, i32, vp, vp, vp]
+    L.sqp_read_stream.argtypes = [vp, sz, i32, vp, vp, vp]
+    L.sqp_rw_stream.argtypes = [vp, sz, vp, i32, i32, vp, vp]
+    L.sqp_clock_rates.argtypes = [vp, vp]
+    dev = torch.device("cuda:0")
+    wall_khz, peak_khz = ctypes.c_int(0), ctypes.c_int(0)
+    if L.sqp_clock_rates(ctypes.byref(wall_khz), ctypes.byref(peak_khz)) != 0:
+        raise RuntimeError("clock-rate query failed")
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+
+    def timed(launch, reps=5):
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(2):
+            if launch(sp) != 0:
+                raise RuntimeError("peak probe launch failed")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            launch(sp)
+        b.record()
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) / reps / 1e3
+        c = clk.cpu().tolist()   # samples of the last launch (its first wave)
+        return sec, (c[1] - c[0]) / (c[3] - c[2]) * wall_khz.value / 1e3
+
+    res = {}
+    blocks, iters = 512, 20000   # 2 blocks of 4 waves per CU: 2 waves per SIMD
+    for fp8, name, per in ((0, "int8_mfma", 65536), (1, "fp8_mfma", 131072)):
+        sec, sclk = timed(lambda sp: L.sqp_mfma_loop(fp8, iters, blocks, sink.data_ptr(),
+                                                      clk.data_ptr(), sp))
+        rate = blocks * 4 * iters * 4 * per / sec / 1e12
+        peak = PEAK_INT8_TOPS if fp8 == 0 else PEAK_FP8_TFLOPS
+        res[name] = {"rate": round(rate, 1), "unit": "TOPS" if fp8 == 0 else "TFLOP/s",
+                     "frac_of_spec": round(rate / peak, 4), "sclk_MHz": round(sclk, 0)}
+    res["clocks_MHz"] = {"wall_counter": wall_khz.value / 1e3, "peak_sclk": peak_khz.value / 1e3}
+    nbytes = 1 << 30
+    x = torch.randint(-(1 << 31), (1 << 31) - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    y = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
+    sec, sclk = timed(lambda sp: L.sqp_read_stream(x.data_ptr(), nbytes, 4096, sink.data_ptr(),
+                                                      clk.data_ptr(), sp))
+    res["hbm_read"] = {"GBs": round(nbytes / sec / 1e9, 1),
+                       "frac_hbm": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+                       "sclk_MHz": round(sclk, 0)}
+    sec, sclk = timed(lambda sp: L.sqp_rw_stream(x.data_ptr(), nbytes, y.data_ptr(), 8192, 1,
+                                                    clk.data_ptr(), sp))
+    res["hbm_rw_2to1"] = {"GBs": round(1.5 * nbytes / sec / 1e9, 1),
+                          "frac_hbm": round(1.5 * nbytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+                          "sclk_MHz": round(sclk, 0)}
+    del x, y
+    return res
+
+
 def extras(torch, L, _sp, T, chk):
     import synth
 
@@ -570,6 +636,7 @@ def extras(torch, L, _sp, T, chk):
         "per_gemm": per, "total_us": round(total_us, 2),
         "TFLOPS": round(total_ops / total_us / 1e6, 1),
         "frac_fp8_peak": round(total_ops / total_us / 1e6 / PEAK_FP8_TFLOPS, 4)}
+    res["measured_peaks"] = measured_peaks(torch)
     return res
 
 
@@ -600,9 +667,19 @@ def cpu_baseline(seconds):
     n = int(max(64, min(28672, n * seconds / max(t, 1e-3))))
     t = run(n)
     ops = 2.0 * M * n * K
+    # the same pass on one thread, on a slice sized for about a quarter of the time
+    oracle.set_num_threads(1)
+    n1 = 64
+    t1 = run(n1)
+    n1 = int(max(64, min(28672, n1 * seconds / 4 / max(t1, 1e-3))))
+    t1 = run(n1)
+    oracle.set_num_threads(0)
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"full a1-a5 pass on X [256,7168] and the first {n} of 28672 output "
-                      f"channels of W ({t:.1f} s)"}
+                      f"channels of W ({t:.1f} s)",
+            "one_thread": {"value": round(2.0 * M * n1 * K / t1 / 1e12, 6), "unit": "TOPS",
+                           "sample": f"the same pass over the first {n1} output channels "
+                                     f"({t1:.1f} s)"}}
 
 
 if __name__ == "__main__":

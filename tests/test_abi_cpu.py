@@ -176,3 +176,16 @@ def test_fp8_validation():
     assert g(FAKE, None, 4, 4, 128, FAKE, 1, FAKE, FAKE, sq.SQ_F16, None) == NULL
     assert g(FAKE, FAKE, 4, 4, 128, FAKE, 1, FAKE, FAKE + 1, sq.SQ_F16, None) == ALIGN
     assert g(None, None, 0, 4, 128, None, 1, None, None, sq.SQ_F16, None) == OK
+
+
+def test_peaks_library_exports_its_header():
+    from w8a8_post_quantization_amd import build as hip_build
+
+    if not os.path.exists(hip_build.PEAKS_LIB_PATH):
+        pytest.skip("libsq_peaks.so not built")
+    P = ctypes.CDLL(hip_build.PEAKS_LIB_PATH)
+    declared = sq.header_functions(os.path.join(os.path.dirname(sq.HEADER), "sq_peaks.h"),
+                                   prefix="sqp_")
+    assert declared == ["sqp_clock_rates", "sqp_mfma_loop", "sqp_read_stream", "sqp_rw_stream"]
+    for name in declared:
+        assert hasattr(P, name), name

@@ -65,11 +65,11 @@ class SQError(RuntimeError):
         super().__init__(f"{fn}: {lib().sq_status_str(status).decode()}")
 
 
-def header_functions(path: str = HEADER):
-    """Names of the functions include/sq.h declares."""
+def header_functions(path: str = HEADER, prefix: str = "sq_"):
+    """Names of the functions a header declares (include/sq.h by default)."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"[a-z0-9_]+)\s*\(", text)))
 
 
 def lib():
