@@ -115,8 +115,9 @@ def _ratio(v):
     return float(v.max() / np.median(v))
 
 
-def sweep(X, W, alphas, mode, backend, sample_rows=256, seed=0):
-    """Rows of dicts, one per alpha (None = no smoothing)."""
+def sweep(X, W, alphas, mode, backend, sample_rows=256, seed=0, X_cal=None):
+    """Rows of dicts, one per alpha (None = no smoothing).  X_cal: the
+    calibration activations the channel maxima come from (default X)."""
     static = mode == STATIC
     M, N = X.shape[0], W.shape[0]
     rng = np.random.default_rng(seed)
@@ -124,7 +125,7 @@ def sweep(X, W, alphas, mode, backend, sample_rows=256, seed=0):
     wr = np.sort(rng.choice(N, size=min(N, 4 * sample_rows), replace=False))
     X64, W64 = _f64(X), _f64(W)
     ref = X64[xr] @ W64.T
-    x_amax = backend.absmax(X)
+    x_amax = backend.absmax(X if X_cal is None else X_cal)
     w_amax = backend.absmax(W)
     out = []
     for a in alphas:
@@ -165,7 +166,34 @@ CONFIGS = {
     "prefill_30b": lambda: synth.prefill_30b(),
     "decoder_1024_q": lambda: {"X": synth.decoder_1024()["X1024"],
                                "W": synth.decoder_1024()["W"]["q"]},
+    "decoder_1024_down": lambda: {"X": synth.decoder_1024()["X3072"],
+                                  "W": synth.decoder_1024()["W"]["down"]},
+    # decode: 32 tokens, the maxima from the 512-token calibration batch
+    "decode_8192_m32": lambda: synth.decode_8192(32),
 }
+
+
+def mixed_errors(X, W, thresholds, backend, sample_rows=256, seed=0):
+    """LLM.int8() on a layer: for each outlier threshold (inf = no outlier
+    columns, the plain vector-wise int8 product) the relative Frobenius
+    error of Y against the fp64 product on sampled rows, and |O|; then the
+    SmoothQuant per-token path (alpha 0.5) on the same layer for comparison."""
+    torch, sq = backend.torch, backend.sq
+    rng = np.random.default_rng(seed)
+    xr = np.sort(rng.choice(X.shape[0], size=min(X.shape[0], sample_rows), replace=False))
+    ref = _f64(X)[xr] @ _f64(W).T
+    xd, wd = backend._d(X), backend._d(W)
+    wq, ws = sq.smooth_weights(wd)
+    out = []
+    for t in thresholds:
+        y, cnt = sq.int8_mixed_matmul(xd, wq, ws, wd, t, out_dtype=torch.float32,
+                                      with_count=True)
+        out.append({"method": f"LLM.int8(), threshold {t}", "n_outliers": int(backend._h(cnt)[0]),
+                    "y_err": _rel(backend._h(y)[xr].astype(np.float64), ref)})
+    row = sweep(X, W, [0.5], TOKEN, backend, sample_rows, seed)[0]
+    out.append({"method": "SmoothQuant, alpha 0.5, per-token", "n_outliers": 0,
+                "y_err": row["y_err"]})
+    return out
 
 
 def markdown(rows, title):
@@ -194,12 +222,23 @@ def main(argv=None):
     for name in names:
         cfg = CONFIGS[name]()
         for mode in modes:
-            rows = sweep(cfg["X"], cfg["W"], alphas, mode, backend, args.rows)
+            rows = sweep(cfg["X"], cfg["W"], alphas, mode, backend, args.rows,
+                         X_cal=cfg.get("X_cal"))
             title = f"{name}, X {'per-tensor static' if mode == STATIC else 'per-token'}"
             if args.json:
                 print(json.dumps({"config": name, "mode": mode, "rows": rows}))
             else:
                 print(markdown(rows, title) + "\n", flush=True)
+    if args.config == "all":
+        cfg = synth.llm_int8_2048()
+        rows = mixed_errors(cfg["X"], cfg["W"], [float("inf"), 6.0], backend, args.rows)
+        if args.json:
+            print(json.dumps({"config": "llm_int8_2048", "rows": rows}))
+        else:
+            lines = ["### llm_int8_2048 (X fp16 [2048,4096], 6 outlier dims of ~20)", "",
+                     "| method | \\|O\\| | y_err |", "|---|---|---|"]
+            lines += [f"| {r['method']} | {r['n_outliers']} | {r['y_err']:.4f} |" for r in rows]
+            print("\n".join(lines) + "\n", flush=True)
     return 0
 
 

@@ -104,3 +104,19 @@ def test_gpu_sweep_matches_oracle_sweep():
         assert g["alpha"] == w["alpha"]
         for k in ("y_err", "x_err", "w_err", "x_zero", "w_zero", "x_ratio", "w_ratio"):
             assert g[k] == pytest.approx(w[k], rel=1e-3, abs=1e-6), (g["alpha"], k)
+
+
+@pytest.mark.gpu
+def test_llm_int8_error_report_on_gpu():
+    """The LLM.int8() rows of the report on a reduced workload: threshold inf
+    keeps no outlier column, 6.0 finds the six planted dimensions, and
+    keeping them in 16-bit lowers the error."""
+    import alpha_sweep
+    import synth
+
+    backend = alpha_sweep.GpuBackend()
+    cfg = synth.llm_int8_2048(M=256, N=512, K=1024)
+    rows = alpha_sweep.mixed_errors(cfg["X"], cfg["W"], [float("inf"), 6.0], backend, 128)
+    assert [r["n_outliers"] for r in rows[:2]] == [0, 6]
+    assert rows[1]["y_err"] < rows[0]["y_err"]
+    assert rows[2]["method"].startswith("SmoothQuant") and 0 < rows[2]["y_err"] < rows[0]["y_err"]
