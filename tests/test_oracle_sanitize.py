@@ -2,7 +2,7 @@
 (gcc, no recovery) and driven through every function on small and edge-case
 shapes (empty M, N or K, one element, a ragged K) by oracle_sanitize_main.c.
 An out-of-bounds access, a leak or undefined behaviour in the oracle makes
-the driver exit non-zero.  CPU only; the sanitizers are host-code tools."""
+the test program exit non-zero.  CPU only; the sanitizers are host-code tools."""
 import os
 import shutil
 import subprocess
