@@ -44,7 +44,8 @@ def _inputs(dt, shape, seed, stream=1, scale=1.0):
 
 @pytest.mark.parametrize("rows,cols,dt", [
     (1, 8, "f16"), (5, 24, "f16"), (37, 520, "f16"), (1000, 7168, "f16"), (16, 1024, "f32"),
-    (300, 68, "f32"), (77, 1032, "bf16"), (4097, 4096, "f16"), (0, 64, "f16")])
+    (300, 68, "f32"), (77, 1032, "bf16"), (4097, 4096, "f16"), (0, 64, "f16"),
+    (256, 520, "f16"), (257, 72, "bf16")])   # the last one-block-per-slab size and the first after
 def test_absmax_parity(torch, rows, cols, dt):
     x = _inputs(dt, (rows, cols), seed=rows + cols, scale=3.0)
     if rows:

@@ -28,11 +28,15 @@ __global__ void fill_zero_u32(uint32_t *p, int64_t n) {
 constexpr int kCvb = 16;           // column vectors per block
 constexpr int kRg = 256 / kCvb;    // row groups per block
 
-template <int DT>
+// DIRECT: one block per column slab covers every row (at most 16 per
+// thread), so the block's maxima are the results: stored (or merged with
+// the running max) without atomics, and the output needs no zero fill.
+template <int DT, bool DIRECT>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           int64_t rows_per_block,
-                                                          uint32_t *__restrict__ out) {
+                                                          uint32_t *__restrict__ out,
+                                                          int accumulate) {
     constexpr int V = Vec<DT>::n;
     __shared__ float red[kRg][kCvb * V + 1];
     const int tid = threadIdx.x, c = tid % kCvb, g = tid / kCvb;
@@ -80,20 +84,38 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
 #pragma unroll
         for (int k = 1; k < kRg; ++k) v = fmaxf(v, red[k][tid]);
         const int64_t col = (int64_t)blockIdx.x * kCvb * V + tid;  // red[.][c*V + i] = column c*V + i
-        if (col < cols && v > 0.0f) atomicMax(&out[col], __float_as_uint(v));
+        if constexpr (DIRECT) {
+            if (col < cols) out[col] = __float_as_uint(accumulate ? fmaxf(v, __uint_as_float(out[col])) : v);
+        } else {
+            if (col < cols && v > 0.0f) atomicMax(&out[col], __float_as_uint(v));
+        }
     }
 }
 
 void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumulate,
                    float *amax, hipStream_t stream) {
     if (cols == 0) return;
+    auto *out = reinterpret_cast<uint32_t *>(amax);
+    auto *xv = reinterpret_cast<const uint4 *>(x);
+    const int V = dt == F32 ? 4 : 8;
+    const int64_t cvec = cols / V;
+    const int64_t bx = (cvec + kCvb - 1) / kCvb;
+    if (rows > 0 && rows <= 16 * kRg) {
+        // Few rows (the activations of a prefill batch): one block per
+        // column slab, direct stores, no fill launch.
+        dim3 grid((unsigned)bx, 1), block(256);
+        if (dt == F32)
+            absmax_cols_kernel<F32, true><<<grid, block, 0, stream>>>(xv, rows, cols, rows, out, accumulate);
+        else if (dt == F16)
+            absmax_cols_kernel<F16, true><<<grid, block, 0, stream>>>(xv, rows, cols, rows, out, accumulate);
+        else
+            absmax_cols_kernel<BF16, true><<<grid, block, 0, stream>>>(xv, rows, cols, rows, out, accumulate);
+        return;
+    }
     if (!accumulate)
         fill_zero_u32<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream>>>(
             reinterpret_cast<uint32_t *>(amax), cols);
     if (rows == 0) return;
-    const int V = dt == F32 ? 4 : 8;
-    const int64_t cvec = cols / V;
-    const int64_t bx = (cvec + kCvb - 1) / kCvb;
     // At most 2048 blocks - one round at 8 blocks per CU, so no block of a
     // second round streams its slab alone at the end - with at least 64
     // rows per block (4 per thread): the blocks of one column slab merge
@@ -106,14 +128,12 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
     const int64_t rpb = (rows + by - 1) / by;
     by = (rows + rpb - 1) / rpb;
     dim3 grid((unsigned)bx, (unsigned)by), block(256);
-    auto *out = reinterpret_cast<uint32_t *>(amax);
-    auto *xv = reinterpret_cast<const uint4 *>(x);
     if (dt == F32)
-        absmax_cols_kernel<F32><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+        absmax_cols_kernel<F32, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
     else if (dt == F16)
-        absmax_cols_kernel<F16><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+        absmax_cols_kernel<F16, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
     else
-        absmax_cols_kernel<BF16><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out);
+        absmax_cols_kernel<BF16, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
 }
 
 __global__ __launch_bounds__(256) void scales_kernel(const float *__restrict__ act_amax,
