@@ -674,7 +674,14 @@ def cpu_baseline(seconds):
     n1 = int(max(64, min(28672, n1 * seconds / 4 / max(t1, 1e-3))))
     t1 = run(n1)
     oracle.set_num_threads(0)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu": model,
             "sample": f"full a1-a5 pass on X [256,7168] and the first {n} of 28672 output "
                       f"channels of W ({t:.1f} s)",
             "one_thread": {"value": round(2.0 * M * n1 * K / t1 / 1e12, 6), "unit": "TOPS",
