@@ -582,13 +582,13 @@ __device__ __forceinline__ void sched_tail() {
 // writes LDS bytes [16 l, 16 l + 16) of its 1 KiB block; the swizzle (see
 // swz) is applied by choosing which global chunk each lane fetches.
 //
-// The rings may differ in depth (STB > STA = 2 prefetches weights further
-// ahead than activations), but loads complete in issue order, so waiting
-// for activation stage kt + 1 also waits for every weight stage issued
-// before it: a deeper weight ring buys no latency.  The shapes used run
-// both rings in lockstep (STB == STA).  Per iteration the kernel issues the
-// activation stage kt + STA, then the weight stage kt + STB, which fixes
-// the vmcnt values below.
+// Both rings have the same depth (STA == STB).  A deeper weight ring buys
+// no latency when the same waves fetch both operands: loads complete in
+// issue order, so waiting for activation stage kt + 1 also waits for every
+// weight stage issued before it (a variant with the ring loads split
+// between waves by operand, and 2 + 4 or 2 + 5 stages, measured no faster).
+// Per iteration the kernel issues the activation stage kt + STA, then the
+// weight stage kt + STB, which fixes the vmcnt values below.
 //
 // Each stage is consumed as four 32-byte quarters with ping-pong fragment
 // registers: a quarter's LDS reads overlap the previous quarter's MFMAs, and
@@ -608,8 +608,8 @@ gemm_pp(GemmArgs p) {
     constexpr int L = LA + LB;
     constexpr int SA = BM * BK, SB = BN * BK;  // bytes of one stage of each operand
     static_assert((NW == 4 || NW == 8) && FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile");
-    static_assert(STA >= 2 && (STB == STA || (STA == 2 && STB > STA)), "ring depths");
-    static_assert((STB - 1) * LB + STA * LA < 64, "vmcnt range");
+    static_assert(STA >= 2 && STB == STA, "ring depths");
+    static_assert(STA * L < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[STA * SA + STB * SB];
     __shared__ __attribute__((aligned(16))) float sx[BM], sw[BN];
@@ -711,20 +711,12 @@ gemm_pp(GemmArgs p) {
                         a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
                 }
         };
-        if constexpr (STB > STA) {
 #pragma unroll
-            for (int s = 0; s < STB; ++s) issue_b(s);
-#pragma unroll
-            for (int s = 0; s < STA; ++s) issue_a(s);
-            wait_vmcnt<(STA - 1) * LA>();
-        } else {
-#pragma unroll
-            for (int s = 0; s < STA; ++s) {
-                issue_a(s);
-                issue_b(s);
-            }
-            wait_vmcnt<(STA - 1) * L>();
+        for (int s = 0; s < STA; ++s) {
+            issue_a(s);
+            issue_b(s);
         }
+        wait_vmcnt<(STA - 1) * L>();
         lds_barrier();
         int4v x0[FM], w0[FN], x1[FM], w1[FN], x2[FM], w2[FN], x3[FM], w3[FN];
         read_frags(0, 0, x0, w0);
@@ -733,12 +725,7 @@ gemm_pp(GemmArgs p) {
             read_frags(kt, 2, x2, w2);
             read_frags(kt, 3, x3, w3);
             mma8(x0, w0, x1, w1);
-            if constexpr (STB > STA) {
-                if (kt == 0) wait_vmcnt<0>();
-                else wait_vmcnt<LB>();
-            } else {
-                wait_vmcnt<(STA - 2) * L>();
-            }
+            wait_vmcnt<(STA - 2) * L>();  // stage kt + 1 of both operands landed
             lds_barrier();  // every wave has read stage kt: its slots are free
             read_frags(kt + 1, 0, x0, w0);
             read_frags(kt + 1, 1, x1, w1);
@@ -763,21 +750,12 @@ gemm_pp(GemmArgs p) {
     constexpr int RQ = FM + FN;  // ds_read_b128 per quarter
     constexpr int MQ = FM * FN;  // MFMAs per quarter
     static_assert(RQ <= MQ, "one read per MFMA slot");
-    if constexpr (STB > STA) {
-        // prologue: all weight stages first, then the activation stages
 #pragma unroll
-        for (int s = 0; s < STB; ++s) issue_b(s);
-#pragma unroll
-        for (int s = 0; s < STA; ++s) issue_a(s);
-        wait_vmcnt<(STA - 1) * LA>();  // A0 (and every B before it) landed
-    } else {
-#pragma unroll
-        for (int s = 0; s < STA; ++s) {
-            issue_a(s);
-            issue_b(s);
-        }
-        wait_vmcnt<(STA - 1) * L>();
+    for (int s = 0; s < STA; ++s) {
+        issue_a(s);
+        issue_b(s);
     }
+    wait_vmcnt<(STA - 1) * L>();
     lds_barrier();
     int4v xa[FM], wa[FN], xb[FM], wb[FN];
     read_frags(0, 0, xa, wa);
@@ -797,14 +775,7 @@ gemm_pp(GemmArgs p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, MQ - RQ, 0);
         }
-        // Stage kt + 1 of both operands must have landed.
-        if constexpr (STB > STA) {
-            // A(kt+1) was the last activation load; after it only B(kt-1+STB)
-            if (kt == 0) wait_vmcnt<0>();
-            else wait_vmcnt<LB>();
-        } else {
-            wait_vmcnt<(STA - 2) * L>();
-        }
+        wait_vmcnt<(STA - 2) * L>();  // stage kt + 1 of both operands landed
         lds_barrier();  // every wave has read stage kt: its slots are free
         read_frags(kt + 1, 0, xa, wa);
         issue_a(kt + STA);
