@@ -200,11 +200,12 @@ def test_gemm_extremal_values(torch):
 
 # The side-term GEMM: 256 x 128 tiles (ragged M and N), 128 x 128 tiles when
 # forced, the non-pipelined tile when K % 128 != 0, more than 32 outlier
-# columns (threshold 0.5: the side operands are staged 32 columns at a time).
+# columns (threshold 0.5: the side operands are staged 32 columns at a time)
+# on each of the three kernels.
 @pytest.mark.parametrize("M,N,K,thr,tile", [
     (300, 200, 512, 6.0, None), (64, 130, 256, float("inf"), None), (40, 96, 128, 0.5, None),
     (2048, 256, 4096, 6.0, None), (300, 200, 512, 6.0, "2"), (100, 150, 208, 6.0, None),
-    (260, 300, 384, 0.5, None)])
+    (260, 300, 384, 0.5, None), (72, 136, 336, 0.5, None), (130, 200, 256, 0.5, "2")])
 def test_mixed_parity(torch, M, N, K, thr, tile):
     import synth
 

@@ -64,48 +64,59 @@ struct GemmArgs {
     int tiles_n;
 };
 
+// LDS layout of a staged chunk of outlier columns, column-major so that one
+// 16-byte read gives four consecutive rows of one column: activation values
+// at xo[t * XS + r], weight values at wo[t * WS + r], wo = xo + 32 * XS.
+template <int BM, int BN>
+struct SideLds {
+    static constexpr int XS = BM + 4, WS = BN + 4;
+    static constexpr int BYTES = 32 * (XS + WS) * 4;
+};
+
 // Stage outlier columns t0 .. t0 + tn - 1 (tn <= 32) of the tile's 16-bit
-// activation rows and weight rows into LDS as floats: xo[r * 33 + t],
-// wo[r * 33 + t], zero for t >= tn.  NT threads; thread tid always serves
-// slot t = tid % 32, so it loads its column index once, and its gathers are
-// unconditional (a clamped column for t >= tn, masked when written): a load
-// under a lane-divergent branch would wait for every earlier load.
+// activation rows and weight rows into LDS as floats (SideLds layout; only
+// columns t < tn are written).  Thread tid serves activation row tid % BM
+// for columns tid / BM, tid / BM + NT / BM, ... and weight row tid % BN for
+// columns tid / BN, tid / BN + NT / BN, ...: the column of each gather is the
+// same across a wave (BM, BN multiples of 64), so its index is one scalar
+// load, dead columns cost no gather, and the loads of a group of four
+// columns are all issued before the first is written.
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *wo, int m0,
                                            int n0, int t0, int tn) {
-    static_assert(NT % 32 == 0 && (BM * 32) % NT == 0 && (BN * 32) % NT == 0, "side staging");
-    constexpr int RX = BM * 32 / NT, RW = BN * 32 / NT;
-    const int tid = threadIdx.x, t = tid & 31, r0 = tid >> 5;
-    const bool live = t < tn;
-    const int64_t col = p.idx[t0 + (live ? t : 0)];
-    // Groups of up to 8 gathers in flight (registers: value and address).
-    constexpr int G = 8;
-    static_assert(RX % G == 0 && RW % G == 0, "gather groups");
-#pragma unroll
-    for (int k0 = 0; k0 < RX; k0 += G) {
-        float v[G];
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int r = r0 + (k0 + k) * (NT / 32);
-            const int gr = m0 + r < p.M ? m0 + r : p.M - 1;
-            v[k] = h2f(p.x16[(int64_t)gr * p.K + col]);
-        }
-#pragma unroll
-        for (int k = 0; k < G; ++k)
-            xo[(r0 + (k0 + k) * (NT / 32)) * 33 + t] = live ? v[k] : 0.0f;
-    }
-#pragma unroll
-    for (int k0 = 0; k0 < RW; k0 += G) {
-        float v[G];
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && NT % BM == 0 && NT % BN == 0,
+                  "side staging");
+    constexpr int PX = NT / BM, PW = NT / BN, G = 4;
+    constexpr int XS = SideLds<BM, BN>::XS, WS = SideLds<BM, BN>::WS;
+    const int tid = threadIdx.x;
+    const int rx = tid % BM, rw = tid % BN;
+    const int cx = __builtin_amdgcn_readfirstlane(tid / BM);
+    const int cw = __builtin_amdgcn_readfirstlane(tid / BN);
+    const uint16_t *xr = p.x16 + (int64_t)(m0 + rx < p.M ? m0 + rx : p.M - 1) * p.K;
+    const uint16_t *wr = p.w16 + (int64_t)(n0 + rw < p.N ? n0 + rw : p.N - 1) * p.K;
+    const int32_t *idx = p.idx + t0;
+    for (int q = 0; q * G * PX < tn || q * G * PW < tn; ++q) {
+        float vx[G], vw[G];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-            const int r = r0 + (k0 + k) * (NT / 32);
-            const int gr = n0 + r < p.N ? n0 + r : p.N - 1;
-            v[k] = h2f(p.w16[(int64_t)gr * p.K + col]);
+            const int t = cx + PX * (q * G + k);
+            vx[k] = t < tn ? h2f(xr[idx[t]]) : 0.0f;
         }
 #pragma unroll
-        for (int k = 0; k < G; ++k)
-            wo[(r0 + (k0 + k) * (NT / 32)) * 33 + t] = live ? v[k] : 0.0f;
+        for (int k = 0; k < G; ++k) {
+            const int t = cw + PW * (q * G + k);
+            vw[k] = t < tn ? h2f(wr[idx[t]]) : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = cx + PX * (q * G + k);
+            if (t < tn) xo[t * XS + rx] = vx[k];
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = cw + PW * (q * G + k);
+            if (t < tn) wo[t * WS + rw] = vw[k];
+        }
     }
 }
 
@@ -139,8 +150,8 @@ struct TileScales {
 // lane l, register v holds row 8*(v/4) + 4*(l/32) + (v%4), column l%32 of
 // the fragment.  With SIDE, the LLM.int8() fp16 side product over the
 // outlier columns is accumulated in ascending column order, staged through
-// LDS 32 columns at a time (rows padded to 33 floats), and added to the
-// dequantized value before narrowing.
+// LDS 32 columns at a time (SideLds), and added to the dequantized value
+// before narrowing.
 //
 // The row and column steps come from LDS (sx[BM], sw[BN]): reading them from
 // global memory inside the store loop would make every iteration wait for
@@ -171,29 +182,37 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) side[i][j][v] = 0.0f;
+        using L = SideLds<BM, BN>;
+        static_assert(L::BYTES <= 2 * (BM + BN) * 128, "side chunk fits the ring");
         float *xo = reinterpret_cast<float *>(smem);
-        float *wo = xo + BM * 33;
+        float *wo = xo + 32 * L::XS;
         const int cnt = *p.count;
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
             stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn);
             __syncthreads();
+            // column by column, so each output still sums in ascending order
+            for (int t = 0; t < tn; ++t) {
+                float wv[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int j = 0; j < FN; ++j) wv[j] = wo[t * L::WS + wn * WTN + j * 32 + fr];
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int rl = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                        const int cl = wn * WTN + j * 32 + fr;
-                        float s = side[i][j][v];
-                        for (int t = 0; t < tn; ++t) {
-                            const float prod = xo[rl * 33 + t] * wo[cl * 33 + t];
-                            s = s + prod;
-                        }
-                        side[i][j][v] = s;
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 x4 = *reinterpret_cast<const float4 *>(
+                            xo + t * L::XS + wm * WTM + i * 32 + 8 * g + 4 * fh);
+                        const float xq[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float prod = xq[q] * wv[j];
+                                side[i][j][4 * g + q] = side[i][j][4 * g + q] + prod;
+                            }
                     }
+            }
         }
     }
 #pragma unroll
@@ -416,29 +435,37 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
             for (int j = 0; j < FM; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) side[i][j][v] = 0.0f;
+        using L = SideLds<BM, BN>;
+        static_assert(L::BYTES <= 2 * (BM + BN) * 128, "side chunk fits the ring");
         float *xo = reinterpret_cast<float *>(smem);
-        float *wo = xo + BM * 33;
+        float *wo = xo + 32 * L::XS;
         const int cnt = *p.count;
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
             stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn);
             __syncthreads();
+            // column by column, so each output still sums in ascending order
+            for (int t = 0; t < tn; ++t) {
+                float xv[FM];
 #pragma unroll
-            for (int i = 0; i < FN; ++i)
+                for (int j = 0; j < FM; ++j) xv[j] = xo[t * L::XS + wm * WTM + j * 32 + fr];
 #pragma unroll
-                for (int j = 0; j < FM; ++j)
+                for (int i = 0; i < FN; ++i)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int nl = wn * WTN + i * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                        const int ml = wm * WTM + j * 32 + fr;
-                        float sum = side[i][j][v];
-                        for (int t = 0; t < tn; ++t) {
-                            const float prod = xo[ml * 33 + t] * wo[nl * 33 + t];
-                            sum = sum + prod;
-                        }
-                        side[i][j][v] = sum;
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 w4 = *reinterpret_cast<const float4 *>(
+                            wo + t * L::WS + wn * WTN + i * 32 + 8 * g + 4 * fh);
+                        const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float prod = xv[j] * wq[q];
+                                side[i][j][4 * g + q] = side[i][j][4 * g + q] + prod;
+                            }
                     }
+            }
         }
     }
     // Exact int32 sums, when asked for (direct stores, not on the fast path).
