@@ -4,10 +4,10 @@
 // ("x_j = max_i |X_ij|" and the weight-side w_j of the SmoothQuant tutorial
 // page, section 缩放因子; the calibration code of the lpnh.cn write-up §3.2).
 // Each thread owns one 16-byte column vector and keeps a running max over a
-// strided slab of rows; a block folds its 16 row groups through LDS and
-// merges into the output with one atomicMax per column on the float bit
-// pattern (non-negative floats order like their unsigned bits).  Reads are
-// coalesced 256-byte row segments; the kernel is HBM-bound.
+// strided slab of rows; a block folds its row groups through LDS and merges
+// into the output with one atomicMax per column on the float bit pattern
+// (non-negative floats order like their unsigned bits).  Reads are
+// coalesced row segments of 256 bytes to 1 KB; the kernel is HBM-bound.
 //
 // compute_scales: s_j = max(max(x_j,1e-5)^a / max(w_j,1e-5)^(1-a), 1e-5),
 // powers and quotient in double rounded once; inv_s = fl(1/s); optional
@@ -22,26 +22,29 @@ __global__ void fill_zero_u32(uint32_t *p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
-// Block = 16 row groups x 16 column vectors: a wave reads four 256-byte row
-// segments per load, thread (g, c) keeps the max of column vector c over
-// rows r0 + g, r0 + g + 16, ... of the block's slab.
-constexpr int kCvb = 16;           // column vectors per block
-constexpr int kRg = 256 / kCvb;    // row groups per block
+// Block = 256 / CVB row groups x CVB column vectors: a wave reads 64 / CVB
+// row segments of 16 CVB bytes per load, thread (g, c) keeps the max of
+// column vector c over rows r0 + g, r0 + g + RG, ... of the block's slab,
+// with U loads in flight.
+constexpr int kCvb = 16;           // column vectors per block (direct path)
+constexpr int kRg = 256 / kCvb;    // row groups per block (direct path)
 
 // DIRECT: one block per column slab covers every row (at most 16 per
 // thread), so the block's maxima are the results: stored (or merged with
 // the running max) without atomics, and the output needs no zero fill.
-template <int DT, bool DIRECT>
+template <int DT, bool DIRECT, int CVB = kCvb, int U = 4>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           int64_t rows_per_block,
                                                           uint32_t *__restrict__ out,
                                                           int accumulate) {
     constexpr int V = Vec<DT>::n;
-    __shared__ float red[kRg][kCvb * V + 1];
-    const int tid = threadIdx.x, c = tid % kCvb, g = tid / kCvb;
+    constexpr int RG = 256 / CVB;
+    static_assert(CVB == 16 || CVB == 32 || CVB == 64, "column vectors per block");
+    __shared__ float red[RG][CVB * V + 1];
+    const int tid = threadIdx.x, c = tid % CVB, g = tid / CVB;
     const int64_t cvec = cols / V;
-    const int64_t cv = (int64_t)blockIdx.x * kCvb + c;
+    const int64_t cv = (int64_t)blockIdx.x * CVB + c;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
 
@@ -52,24 +55,19 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
     if (cv < cvec) {
         const uint4 *p = x + cv;
         int64_t r = r0 + g;
-        for (; r + 3 * kRg < r1; r += 4 * kRg) {
-            uint4 v0 = ld_nt(p + r * cvec), v1 = ld_nt(p + (r + kRg) * cvec);
-            uint4 v2 = ld_nt(p + (r + 2 * kRg) * cvec), v3 = ld_nt(p + (r + 3 * kRg) * cvec);
-            float f[V];
-            widen16<DT>(v0, f);
+        for (; r + (U - 1) * RG < r1; r += U * RG) {
+            uint4 v[U];
 #pragma unroll
-            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
-            widen16<DT>(v1, f);
+            for (int u = 0; u < U; ++u) v[u] = ld_nt(p + (r + u * RG) * cvec);
 #pragma unroll
-            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
-            widen16<DT>(v2, f);
+            for (int u = 0; u < U; ++u) {
+                float f[V];
+                widen16<DT>(v[u], f);
 #pragma unroll
-            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
-            widen16<DT>(v3, f);
-#pragma unroll
-            for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+                for (int i = 0; i < V; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+            }
         }
-        for (; r < r1; r += kRg) {
+        for (; r < r1; r += RG) {
             float f[V];
             widen16<DT>(ld_nt(p + r * cvec), f);
 #pragma unroll
@@ -79,11 +77,11 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const uint4 *__restric
 #pragma unroll
     for (int i = 0; i < V; ++i) red[g][c * V + i] = m[i];
     __syncthreads();
-    if (tid < kCvb * V) {
-        float v = red[0][tid];
+    for (int t = tid; t < CVB * V; t += 256) {
+        float v = red[0][t];
 #pragma unroll
-        for (int k = 1; k < kRg; ++k) v = fmaxf(v, red[k][tid]);
-        const int64_t col = (int64_t)blockIdx.x * kCvb * V + tid;  // red[.][c*V + i] = column c*V + i
+        for (int k = 1; k < RG; ++k) v = fmaxf(v, red[k][t]);
+        const int64_t col = (int64_t)blockIdx.x * CVB * V + t;  // red[.][c*V + i] = column c*V + i
         if constexpr (DIRECT) {
             if (col < cols) out[col] = __float_as_uint(accumulate ? fmaxf(v, __uint_as_float(out[col])) : v);
         } else {
@@ -116,24 +114,29 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
         fill_zero_u32<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream>>>(
             reinterpret_cast<uint32_t *>(amax), cols);
     if (rows == 0) return;
+    // 64 column vectors per block (a wave reads one 1 KB row segment per
+    // load), 8 loads in flight per thread: W [28672, 7168] fp16 63-64 us
+    // against 69 us with 16 x 4 (four 256-byte segments per wave load).
+    constexpr int CVB = 64, U = 8;
+    const int64_t bxw = (cvec + CVB - 1) / CVB;
     // At most 2048 blocks - one round at 8 blocks per CU, so no block of a
     // second round streams its slab alone at the end - with at least 64
-    // rows per block (4 per thread): the blocks of one column slab merge
+    // rows per block: the blocks of one column slab merge
     // with one atomicMax per column each, so their number is kept small.
-    int64_t by = 2048 / bx;
+    int64_t by = 2048 / bxw;
     const int64_t max_by = (rows + 63) / 64;
     if (by > max_by) by = max_by;
     if (by > 65535) by = 65535;
     if (by < 1) by = 1;
     const int64_t rpb = (rows + by - 1) / by;
     by = (rows + rpb - 1) / rpb;
-    dim3 grid((unsigned)bx, (unsigned)by), block(256);
+    dim3 grid((unsigned)bxw, (unsigned)by), block(256);
     if (dt == F32)
-        absmax_cols_kernel<F32, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
+        absmax_cols_kernel<F32, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
     else if (dt == F16)
-        absmax_cols_kernel<F16, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
+        absmax_cols_kernel<F16, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
     else
-        absmax_cols_kernel<BF16, false><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
+        absmax_cols_kernel<BF16, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
 }
 
 __global__ __launch_bounds__(256) void scales_kernel(const float *__restrict__ act_amax,
