@@ -45,7 +45,9 @@ def _inputs(dt, shape, seed, stream=1, scale=1.0):
 @pytest.mark.parametrize("rows,cols,dt", [
     (1, 8, "f16"), (5, 24, "f16"), (37, 520, "f16"), (1000, 7168, "f16"), (16, 1024, "f32"),
     (300, 68, "f32"), (77, 1032, "bf16"), (4097, 4096, "f16"), (0, 64, "f16"),
-    (256, 520, "f16"), (257, 72, "bf16")])   # the last one-block-per-slab size and the first after
+    (256, 520, "f16"), (257, 72, "bf16"),    # the last one-block-per-slab size and the first after
+    # wide slabs (64 column vectors, >= 1024 blocks), a ragged last slab and row block
+    (8001, 4104, "f16"), (9000, 2052, "f32"), (6001, 8200, "bf16")])
 def test_absmax_parity(torch, rows, cols, dt):
     x = _inputs(dt, (rows, cols), seed=rows + cols, scale=3.0)
     if rows:

@@ -114,29 +114,44 @@ void launch_absmax(const void *x, int dt, int64_t rows, int64_t cols, int accumu
         fill_zero_u32<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream>>>(
             reinterpret_cast<uint32_t *>(amax), cols);
     if (rows == 0) return;
-    // 64 column vectors per block (a wave reads one 1 KB row segment per
-    // load), 8 loads in flight per thread: W [28672, 7168] fp16 63-64 us
-    // against 69 us with 16 x 4 (four 256-byte segments per wave load).
-    constexpr int CVB = 64, U = 8;
-    const int64_t bxw = (cvec + CVB - 1) / CVB;
     // At most 2048 blocks - one round at 8 blocks per CU, so no block of a
     // second round streams its slab alone at the end - with at least 64
-    // rows per block: the blocks of one column slab merge
-    // with one atomicMax per column each, so their number is kept small.
-    int64_t by = 2048 / bxw;
-    const int64_t max_by = (rows + 63) / 64;
-    if (by > max_by) by = max_by;
-    if (by > 65535) by = 65535;
-    if (by < 1) by = 1;
-    const int64_t rpb = (rows + by - 1) / by;
-    by = (rows + rpb - 1) / rpb;
-    dim3 grid((unsigned)bxw, (unsigned)by), block(256);
-    if (dt == F32)
-        absmax_cols_kernel<F32, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
-    else if (dt == F16)
-        absmax_cols_kernel<F16, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
-    else
-        absmax_cols_kernel<BF16, false, CVB, U><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, out, 0);
+    // rows per block: the blocks of one column slab merge with one
+    // atomicMax per column each, so their number is kept small.
+    auto shape = [&](int64_t cvb, int64_t &gx, int64_t &gy, int64_t &rpb) {
+        gx = (cvec + cvb - 1) / cvb;
+        gy = 2048 / gx;
+        const int64_t max_by = (rows + 63) / 64;
+        if (gy > max_by) gy = max_by;
+        if (gy > 65535) gy = 65535;
+        if (gy < 1) gy = 1;
+        rpb = (rows + gy - 1) / gy;
+        gy = (rows + rpb - 1) / rpb;
+    };
+    // 64 column vectors per block (a wave reads one 1 KB row segment per
+    // load) with 8 loads in flight per thread where the rows are at least
+    // 64 vectors wide and that still gives at least 1024 blocks: W [28672, 7168] fp16 63-64 us against 69 us with
+    // 16 x 4 (four 256-byte segments per wave load).  Smaller inputs keep
+    // 16 x 4, whose blocks are four times as many: X [2048, 4096] gets 1024
+    // blocks instead of 256 (LLM.int8() outlier detection: 4 us less).
+    int64_t gx, gy, rpb;
+    shape(64, gx, gy, rpb);
+    const bool wide = cvec >= 64 && gx * gy >= 1024;
+    if (!wide) shape(kCvb, gx, gy, rpb);
+    dim3 grid((unsigned)gx, (unsigned)gy), block(256);
+#define SQ_ABS(DTV)                                                                              \
+    do {                                                                                         \
+        if (wide)                                                                                \
+            absmax_cols_kernel<DTV, false, 64, 8><<<grid, block, 0, stream>>>(xv, rows, cols, rpb, \
+                                                                              out, 0);           \
+        else                                                                                     \
+            absmax_cols_kernel<DTV, false, kCvb, 4><<<grid, block, 0, stream>>>(xv, rows, cols,  \
+                                                                                rpb, out, 0);    \
+    } while (0)
+    if (dt == F32) SQ_ABS(F32);
+    else if (dt == F16) SQ_ABS(F16);
+    else SQ_ABS(BF16);
+#undef SQ_ABS
 }
 
 __global__ __launch_bounds__(256) void scales_kernel(const float *__restrict__ act_amax,
