@@ -204,17 +204,21 @@ def test_gemm_extremal_values(torch):
 # forced, the non-pipelined tile when K % 128 != 0, more than 32 outlier
 # columns (threshold 0.5: the side operands are staged 32 columns at a time)
 # on each of the three kernels.
-@pytest.mark.parametrize("M,N,K,thr,tile", [
-    (300, 200, 512, 6.0, None), (64, 130, 256, float("inf"), None), (40, 96, 128, 0.5, None),
-    (2048, 256, 4096, 6.0, None), (300, 200, 512, 6.0, "2"), (100, 150, 208, 6.0, None),
-    (260, 300, 384, 0.5, None), (72, 136, 336, 0.5, None), (130, 200, 256, 0.5, "2")])
-def test_mixed_parity(torch, M, N, K, thr, tile):
+@pytest.mark.parametrize("M,N,K,thr,tile,n_dims", [
+    (300, 200, 512, 6.0, None, 6), (64, 130, 256, float("inf"), None, 6),
+    (40, 96, 128, 0.5, None, 6), (2048, 256, 4096, 6.0, None, 6), (300, 200, 512, 6.0, "2", 6),
+    (100, 150, 208, 6.0, None, 6), (260, 300, 384, 0.5, None, 6), (72, 136, 336, 0.5, None, 6),
+    (130, 200, 256, 0.5, "2", 6),
+    # |O| at the 32-column chunk boundary and one past it (planted dimensions)
+    (300, 200, 512, 6.0, None, 32), (300, 200, 512, 6.0, None, 33),
+    (100, 150, 208, 6.0, None, 33)])
+def test_mixed_parity(torch, M, N, K, thr, tile, n_dims):
     import synth
 
-    cfg = synth.llm_int8_2048(M=M, N=N, K=K)
+    cfg = synth.llm_int8_2048(M=M, N=N, K=K, n_dims=n_dims)
     X, W = cfg["X"], cfg["W"]
     wq_o, ws_o = oracle.smooth_weights(W, None)
-    log(f"mixed M={M} N={N} K={K} thr={thr} tile={tile}")
+    log(f"mixed M={M} N={N} K={K} thr={thr} tile={tile} n_dims={n_dims}")
     wq, ws = sq.smooth_weights(dev(W, torch))
     assert_bits_equal(host(wq, torch), wq_o, "wq")
     if tile is not None:
