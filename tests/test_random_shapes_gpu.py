@@ -104,3 +104,36 @@ def test_chain_random_shape(torch, i):
     xq8_o, xs8_o = oracle.quantize_act_fp8(X, inv_o, mode, st8_o)
     assert_bits_equal(host(xs8, torch), xs8_o, "x_scale e4m3")
     assert_bits_equal(host(xq8, torch), xq8_o, "xq e4m3")
+
+
+N_MIXED = 16
+
+
+def _mixed_case(i):
+    r = np.random.default_rng(9500 + i)
+    M = int(r.integers(1, 40)) if i % 4 == 0 else int(r.integers(40, 600))
+    N = int(r.integers(1, 500))
+    K = 128 * int(r.integers(1, 12)) if i % 2 == 0 else 16 * int(r.integers(1, 100))
+    n_dims = int(r.choice([0, 1, 3, 6, 31, 32, 33, 40]))
+    return dict(M=M, N=N, K=K, n_dims=min(n_dims, K), thr=float(r.choice([6.0, 6.0, 10.0])),
+                ydt=("f16", "f32", "bf16")[i % 3], seed=200 + i)
+
+
+@pytest.mark.parametrize("i", range(N_MIXED))
+def test_mixed_random_shape(torch, i):
+    """LLM.int8() (a6) on seeded random shapes: |O| from 0 to 40 planted
+    dimensions (across the 32-column staging chunks), ragged M and N, K with
+    and without whole 128-byte stages, every output type; |O| and y
+    bit-exact against the oracle given the oracle's weight quantization."""
+    c = _mixed_case(i)
+    log(f"mixed random case {i}: {c}")
+    cfg = synth.llm_int8_2048(M=c["M"], N=c["N"], K=c["K"], seed=c["seed"], n_dims=c["n_dims"])
+    X, W = cfg["X"], cfg["W"]
+    wq_o, ws_o = oracle.smooth_weights(W, None)
+    ydt = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[c["ydt"]]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[c["ydt"]]
+    y, cnt = sq.int8_mixed_matmul(dev(X, torch), dev(wq_o, torch), dev(ws_o, torch),
+                                  dev(W, torch), c["thr"], out_dtype=tdt, with_count=True)
+    r = oracle.int8_mixed_matmul(X, wq_o, ws_o, W, c["thr"], y_dt=ydt)
+    assert int(host(cnt, torch)[0]) == r["idx"].size
+    assert_bits_equal(host(y, torch), r["y"], "y")
