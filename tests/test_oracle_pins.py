@@ -393,6 +393,98 @@ def test_mixed_single_outlier_side_is_exact(orc):
     assert np.array_equal(r["acc"], r["xq"].astype(np.int64) @ wq.astype(np.int64).T)
 
 
+def test_mixed_row_step_excludes_outlier_columns(orc):
+    """[INT8-expl] §2.2 decomposition: the int8 path quantizes x[:, mask], the
+    columns that are not outlier dims, so a row's step comes from those
+    columns only and the outlier columns contribute no codes.  Worked by
+    hand: column 5 (7, -9.5, 0.25) reaches 6 and is an outlier dim; column 9
+    (1, 2, -3) does not.  Row 0's non-outlier maximum is 1 (not 7): step
+    1/127 and code 127 at column 9; rows 1 and 2 have maxima 2 and 3.  The
+    weights are quantized per output channel over all K: row 0 (0.5 and 1)
+    has step 1/127 and codes 64 (127 * 0.5 = 63.5, half to even) and 127;
+    row 1 (-0.125, 1) codes -16 (-15.875) and 127; row 2 (3, 1) step 3/127,
+    codes 127 and 42 (127 / 3 = 42.33); row 3 (0, 1) code 127."""
+    X = np.zeros((3, 64), np.float16)
+    X[:, 5] = np.array([7.0, -9.5, 0.25], np.float16)
+    X[:, 9] = np.array([1.0, 2.0, -3.0], np.float16)
+    W = np.zeros((4, 64), np.float16)
+    W[:, 5] = np.array([0.5, -0.125, 3.0, 0.0], np.float16)
+    W[:, 9] = np.array([1.0, 1.0, 1.0, 1.0], np.float16)
+    wq, ws = orc.smooth_weights(W, None)
+    assert list(wq[:, 5]) == [64, -16, 127, 0] and list(wq[:, 9]) == [127, 127, 42, 127]
+    f = np.float32
+    assert list(ws) == [f(1) / f(127), f(1) / f(127), f(3) / f(127), f(1) / f(127)]
+    r = orc.int8_mixed_matmul(X, wq, ws, W, 6.0, y_dt=orc.F32)
+    assert list(r["idx"]) == [5]
+    assert list(r["x_scale"]) == [f(1) / f(127), f(2) / f(127), f(3) / f(127)]
+    want_xq = np.zeros((3, 64), np.int8)
+    want_xq[:, 9] = [127, 127, -127]
+    assert np.array_equal(r["xq"], want_xq)          # column 5 carries no code
+    assert r["acc"].tolist() == [[16129, 16129, 5334, 16129], [16129, 16129, 5334, 16129],
+                                 [-16129, -16129, -5334, -16129]]
+
+
+def test_mixed_merge_rounds_once(orc):
+    """[INT8-expl] §2.2 adds the 16-bit side result and the int8 result into
+    one 16-bit output; the reading here forms fl(dequant + side) in fp32 and
+    rounds to fp16 once.  Worked by hand: non-outlier row maximum 127/64
+    gives step 2^-6 and codes x * 64; weight row maximum 127/32 gives step
+    2^-5 and codes w * 32; the int8 sum 127 * 16 + 17 * 1 = 2049 dequantizes
+    exactly to 2049 * 2^-11 = 1 + 2^-11; the outlier dim (x = 8) times
+    w = 2^-14 gives side = 2^-11.  One rounding: 1 + 2^-10 exactly.  Rounding
+    the dequantized value to fp16 first (1 + 2^-11 is a tie: 1.0) and then
+    adding gives 1.0."""
+    K = 64
+    X = np.zeros((1, K), np.float16)
+    X[0, 0] = 127 / 64          # q = 127
+    X[0, 1] = 17 / 64           # q = 17
+    X[0, 3] = 8.0               # the outlier dim
+    W = np.zeros((1, K), np.float16)
+    W[0, 0] = 0.5               # q = 16
+    W[0, 1] = 1 / 32            # q = 1
+    W[0, 2] = 127 / 32          # the row maximum, q = 127 (X is 0 there)
+    W[0, 3] = 2.0 ** -14
+    wq, ws = orc.smooth_weights(W, None)
+    assert ws[0] == 2.0 ** -5 and list(wq[0, :3]) == [16, 1, 127]
+    r = orc.int8_mixed_matmul(X, wq, ws, W, 6.0, y_dt=orc.F16)
+    assert list(r["idx"]) == [3]
+    assert r["x_scale"][0] == 2.0 ** -6
+    assert r["acc"][0, 0] == 2049
+    assert r["y"][0, 0] == np.float16(1 + 2.0 ** -10)
+    assert np.float16(np.float16(1 + 2.0 ** -11) + np.float16(2.0 ** -11)) == 1.0  # the other order
+
+
+def test_mixed_side_sums_in_ascending_column_order(orc):
+    """The side term accumulates the outlier dims in ascending column order
+    from 0 in fp32.  Worked by hand with a zero int8 part: products 2^10
+    (column 2), 2^-14 (column 5), 2^-14 (column 7).  Ascending:
+    2^10 + 2^-14 is a tie at fp32's 2^-13 spacing and rounds to 2^10, twice:
+    the sum is 2^10.  Any order that adds the two small products first gives
+    2^10 + 2^-13."""
+    K = 16
+    X = np.zeros((1, K), np.float16)
+    W = np.zeros((2, K), np.float16)
+    X[0, [2, 5, 7]] = 8.0
+    W[0, 2], W[0, 5], W[0, 7] = 128.0, 2.0 ** -17, 2.0 ** -17
+    W[1, 2], W[1, 5], W[1, 7] = 2.0 ** -17, 2.0 ** -17, 128.0   # the big product last
+    wq, ws = orc.smooth_weights(W, None)
+    r = orc.int8_mixed_matmul(X, wq, ws, W, 6.0, y_dt=orc.F32)
+    assert list(r["idx"]) == [2, 5, 7]
+    assert not r["xq"].any() and not r["acc"].any()
+    assert r["y"][0, 0] == np.float32(2.0 ** 10)
+    assert r["y"][0, 1] == np.float32(2.0 ** 10 + 2.0 ** -13)
+
+
+def test_mixed_threshold_is_inclusive(orc):
+    """[INT8-expl] §4.1: a value reaching the threshold marks its dimension:
+    |x| = 6.0 is an outlier, 5.99609375 (the fp16 value just below) is not."""
+    X = np.zeros((2, 16), np.float16)
+    X[0, 4] = -6.0
+    X[1, 11] = 5.99609375
+    X[1, 12] = 6.0
+    assert list(orc.outlier_columns(X, 6.0)) == [4, 12]
+
+
 def test_mixed_prep_and_sampled(orc, syn):
     cfg = syn.llm_int8_2048(M=128, N=96, K=256)
     X, W = cfg["X"], cfg["W"]
