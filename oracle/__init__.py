@@ -81,10 +81,9 @@ def lib():
             "orc_smooth_weights_fp8": (None, [_P, _I, _I64, _I64, _P, _P, _P]),
             "orc_quantize_act_fp8": (None, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P]),
             "orc_static_scale": (None, [_P, _P, _I64, _F, _P]),
-            "orc_gemm_fp8_dequant": (None, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P,
-                                            _P, _P]),
+            "orc_gemm_fp8_dequant": (None, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P]),
             "orc_gemm_fp8_dequant_at": (None, [_P, _P, _I64, _P, _I, _P, _I, _P, _P, _I64, _P,
-                                               _P, _P, _P]),
+                                               _P]),
             "orc_norm_stats": (None, [_P, _I64, _I64, _I, _F, _P, _P]),
             "orc_norm_quantize": (None, [_P, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
         }
@@ -432,8 +431,7 @@ def static_scale(act_amax, inv_s, qmax):
 
 
 def gemm_fp8_dequant(xq, wq, x_scale, w_scale, y_dt=F32, per_row=1):
-    """(y, acc, abs_sum, blk_sum): acc the exact fp64 sum, abs_sum = sum
-    |products|, blk_sum = sum over 64-term blocks of the block's max |p|."""
+    """(y, acc): acc the exact fp64 sum of the e4m3 products."""
     xq, wq = _c(xq), _c(wq)
     M, K = xq.shape
     N = wq.shape[0]
@@ -441,12 +439,10 @@ def gemm_fp8_dequant(xq, wq, x_scale, w_scale, y_dt=F32, per_row=1):
     w_scale = _c(np.asarray(w_scale, np.float32))
     y = _out((M, N), y_dt)
     acc = np.empty((M, N), np.float64)
-    ab = np.empty((M, N), np.float64)
-    bs = np.empty((M, N), np.float64)
     lib().orc_gemm_fp8_dequant(xq.ctypes.data, wq.ctypes.data, M, N, K, x_scale.ctypes.data,
                                per_row, w_scale.ctypes.data, y.ctypes.data, y_dt,
-                               acc.ctypes.data, ab.ctypes.data, bs.ctypes.data)
-    return y, acc, ab, bs
+                               acc.ctypes.data)
+    return y, acc
 
 
 def gemm_fp8_dequant_at(xq, wq, x_scale, w_scale, rows, cols, y_dt=F32, per_row=1):
@@ -459,10 +455,7 @@ def gemm_fp8_dequant_at(xq, wq, x_scale, w_scale, rows, cols, y_dt=F32, per_row=
     n = rows.size
     y = _out((n,), y_dt)
     acc = np.empty(n, np.float64)
-    ab = np.empty(n, np.float64)
-    bs = np.empty(n, np.float64)
     lib().orc_gemm_fp8_dequant_at(xq.ctypes.data, wq.ctypes.data, K, x_scale.ctypes.data,
                                   per_row, w_scale.ctypes.data, y_dt, rows.ctypes.data,
-                                  cols.ctypes.data, n, y.ctypes.data, acc.ctypes.data,
-                                  ab.ctypes.data, bs.ctypes.data)
-    return y, acc, ab, bs
+                                  cols.ctypes.data, n, y.ctypes.data, acc.ctypes.data)
+    return y, acc

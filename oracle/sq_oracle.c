@@ -613,38 +613,25 @@ static void fp8_table_init(void) {
     for (int i = 0; i < 256; ++i) fp8_table[i] = (double)orc_fp8_decode((uint8_t)i);
 }
 
-static void dot_fp8(const uint8_t *a, const uint8_t *b, int64_t K, double *acc,
-                    double *abs_sum, double *blk_sum) {
-    double s = 0.0, t = 0.0, bs = 0.0, bm = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-        double p = fp8_table[a[k]] * fp8_table[b[k]];
-        s += p;
-        t += fabs(p);
-        if (fabs(p) > bm) bm = fabs(p);
-        if (k % 64 == 63 || k == K - 1) {
-            bs += bm;
-            bm = 0.0;
-        }
-    }
-    *acc = s;
-    *abs_sum = t;
-    *blk_sum = bs;
+/* The exact sum of the products in double: every e4m3 product is a multiple
+ * of 2^-18 below 2^18, so K <= 2^16 terms need fewer than 53 bits and no
+ * addition rounds. */
+static double dot_fp8(const uint8_t *a, const uint8_t *b, int64_t K) {
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += fp8_table[a[k]] * fp8_table[b[k]];
+    return s;
 }
 
 void orc_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
                           int64_t K, const float *x_scale, int per_row,
-                          const float *w_scale, void *y, int y_dt, double *acc_out,
-                          double *abs_out, double *blk_out) {
+                          const float *w_scale, void *y, int y_dt, double *acc_out) {
     fp8_table_init();
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float dx = x_scale[per_row ? m : 0];
         for (int64_t n = 0; n < N; ++n) {
-            double acc, abs_sum, blk_sum;
-            dot_fp8(xq + m * K, wq + n * K, K, &acc, &abs_sum, &blk_sum);
+            double acc = dot_fp8(xq + m * K, wq + n * K, K);
             if (acc_out) acc_out[m * N + n] = acc;
-            if (abs_out) abs_out[m * N + n] = abs_sum;
-            if (blk_out) blk_out[m * N + n] = blk_sum;
             float c = dx * w_scale[n];
             if (y) store_elem(y, y_dt, m * N + n, (float)acc * c);
         }
@@ -654,17 +641,13 @@ void orc_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64
 void orc_gemm_fp8_dequant_at(const uint8_t *xq, const uint8_t *wq, int64_t K,
                              const float *x_scale, int per_row, const float *w_scale,
                              int y_dt, const int64_t *rows, const int64_t *cols,
-                             int64_t n, void *y, double *acc_out, double *abs_out,
-                             double *blk_out) {
+                             int64_t n, void *y, double *acc_out) {
     fp8_table_init();
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         int64_t m = rows[i], c = cols[i];
-        double acc, abs_sum, blk_sum;
-        dot_fp8(xq + m * K, wq + c * K, K, &acc, &abs_sum, &blk_sum);
+        double acc = dot_fp8(xq + m * K, wq + c * K, K);
         if (acc_out) acc_out[i] = acc;
-        if (abs_out) abs_out[i] = abs_sum;
-        if (blk_out) blk_out[i] = blk_sum;
         float cc = x_scale[per_row ? m : 0] * w_scale[c];
         if (y) store_elem(y, y_dt, i, (float)acc * cc);
     }

@@ -99,17 +99,15 @@ static void run_shape(int64_t M, int64_t N, int64_t K) {
     orc_quantize_act_fp8(x, ORC_F32, M, K, inv, ORC_PER_TOKEN_DYNAMIC, NULL, xq8, xsc);
     orc_quantize_act_fp8(x16, ORC_F16, M, K, NULL, ORC_PER_TENSOR_STATIC, st8, xq8, xsc);
     double *a64 = malloc(MN * sizeof(double));
-    double *b64 = malloc(MN * sizeof(double));
-    double *c64 = malloc(MN * sizeof(double));
-    orc_gemm_fp8_dequant(xq8, wq8, M, N, K, xsc, 0, wsc, y, ORC_F32, a64, b64, c64);
-    orc_gemm_fp8_dequant(xq8, wq8, M, N, K, xsc, 0, wsc, y, ORC_BF16, NULL, NULL, NULL);
+    orc_gemm_fp8_dequant(xq8, wq8, M, N, K, xsc, 0, wsc, y, ORC_F32, a64);
+    orc_gemm_fp8_dequant(xq8, wq8, M, N, K, xsc, 0, wsc, y, ORC_BF16, NULL);
     if (M > 0 && N > 0)
-        orc_gemm_fp8_dequant_at(xq8, wq8, K, xsc, 0, wsc, ORC_F16, rows, cols, 3, y, a64, b64, c64);
+        orc_gemm_fp8_dequant_at(xq8, wq8, K, xsc, 0, wsc, ORC_F16, rows, cols, 3, y, a64);
 
     free(x); free(w); free(x16); free(w16); free(xa); free(wa); free(s); free(inv);
     free(ws32); free(wq); free(xq); free(wsc); free(xsc); free(rm); free(y); free(acc);
     free(idx); free(y64); free(g); free(b); free(g2); free(b2); free(mu); free(rs); free(yo);
-    free(xq8); free(wq8); free(a64); free(b64); free(c64);
+    free(xq8); free(wq8); free(a64);
 }
 
 int main(void) {
