@@ -192,7 +192,7 @@ def profile_gemms():
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     for _ in range(3):
         chk(L.sq_int8_mixed_matmul(P(x), M, K, P(wq), P(ws), P(w16), N, 6.0, P(work), need, P(y), 1,
-                                   None, sp), "llm_int8")
+                                   None, None, sp), "llm_int8")
     torch.cuda.synchronize()
     ran.append("llm_int8")
     print(json.dumps({"profile_gemms": ran}), flush=True)
@@ -578,7 +578,8 @@ def extras(torch, L, _sp, T, chk):
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     us = _time_loop(torch, [lambda: chk(L.sq_int8_mixed_matmul(
-        P(Xm), M, K, P(wq), P(ws), P(Wm), N, 6.0, P(wsp), need, P(y), 1, P(cnt), sp), "mixed")],
+        P(Xm), M, K, P(wq), P(ws), P(Wm), N, 6.0, P(wsp), need, P(y), 1, None, P(cnt), sp),
+        "mixed")],
         20)
     res["llm_int8_2048"] = {"us": round(us, 2), "n_outliers": int(cnt.item()),
                             "TOPS": round(2.0 * M * N * K / us / 1e6, 1)}

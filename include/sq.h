@@ -24,7 +24,10 @@
  *    before anything is enqueued and leave all outputs untouched.  A failed
  *    launch returns SQ_ERR_HIP (hipGetLastError after the launch).
  *  - Sizes are int64_t; 0 rows/tokens/outputs is allowed and enqueues
- *    nothing (except where stated).  Row strides must be multiples of 16
+ *    nothing (except where stated).  A row length or inner dimension K of 0
+ *    with at least one row (or output) is rejected with SQ_ERR_SHAPE before
+ *    any pointer is used: there is no row to quantize and no sum to form.
+ *    Row strides must be multiples of 16
  *    bytes and int8 / 16-bit / fp32 tensor pointers 16-byte aligned, so the
  *    kernels can move 16-byte vectors: K % 16 == 0 for int8 operands,
  *    cols % 8 == 0 (16-bit) or cols % 4 == 0 (fp32) for reductions.
@@ -108,7 +111,7 @@ int sq_compute_scales(const float *act_amax, const float *w_amax, int64_t K,
  *   wq      [N, K] int8 out: w' = fl(W * s); a_n = max(max_k |w'|, 1e-8);
  *           q = clamp(round_half_even(fl(w' * fl(127 / a_n))), -127, 127)
  *   w_scale [N] fp32 out: fl(a_n / 127)
- * K % 16 == 0.
+ * K % 16 == 0; K > 0 when N > 0.
  */
 int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
                       const float *s, int8_t *wq, float *w_scale, void *stream);
@@ -127,7 +130,7 @@ int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K,
  *   xq           [M, K] int8 out; x_scale [M] (dynamic) or [1] (static) out
  *                (with M == 0 in dynamic mode nothing is written and x_scale
  *                may be NULL; in static mode x_scale[0] is still set)
- * K % 16 == 0.
+ * K % 16 == 0; K > 0 when M > 0.
  */
 int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
                     const float *inv_s, int mode, const float *static_scale,
@@ -145,7 +148,8 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K,
  *   s        [K] fp32, or NULL (this layer's columns unscaled)
  *   wq, w_scale as sq_smooth_weights, of w''[n, k] = fl(fl(w * row_mul[n]) * s[k]).
  * The next layer then quantizes its input with inv_s = NULL (the division
- * already happened here).  K % 16 == 0; row_mul 4-byte aligned.
+ * already happened here).  K % 16 == 0 (K > 0 when N > 0); row_mul 4-byte
+ * aligned.
  */
 int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K,
                              const float *row_mul, const float *s, int8_t *wq,
@@ -174,7 +178,7 @@ int sq_static_scale(const float *act_amax, const float *inv_s, int64_t K, float 
  *                          static_scale as sq_quantize_act (the static pair
  *                          from sq_static_scale with qmax 448) -> xq [M, K]
  *                          e4m3, x_scale [M] or [1].
- * K % 16 == 0.
+ * K % 16 == 0; K > 0 when there are rows.
  */
 int sq_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K, const float *s,
                           uint8_t *wq, float *w_scale, void *stream);
@@ -209,7 +213,8 @@ int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
  *   y  [M, N] of y_dt out: acc = sum_k xq[m,k] * wq[n,k] (exact int32),
  *      y = fl(fl((float)acc) * fl(x_scale[m] * w_scale[n])) narrowed RNE.
  *   acc_out [M, N] int32 out or NULL (the integer sums, for checking).
- * K % 16 == 0; |acc| must fit int32 (holds for K <= 133143).  M <= 32 uses
+ * K % 16 == 0, K > 0 when M, N > 0; |acc| must fit int32 (holds for
+ * K <= 133143).  M <= 32 uses
  * the skinny (decode) kernel, larger M the tiled MFMA kernel; both give the
  * same bits.
  */
@@ -232,19 +237,26 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M,
  *     no smoothing); acc = X~q . wq^T;
  *     side = sum over o in O ascending of fl(x[m,o] * w[n,o]) in fp32 from 0;
  *     y = fl(fl((float)acc * fl(dx_m * dw_n)) + side), narrowed RNE.
+ *   acc_out   [M, N] int32 out or NULL: the int8 sums acc (for checking).
  *   n_outliers_out  device int32 out or NULL: |O|.
  *   workspace       device memory of at least
  *                   sq_int8_mixed_matmul_workspace(M, K) bytes, 256-byte
- *                   aligned; it holds X~q, the row steps, the column mask
- *                   and the O list.  Contents on return are unspecified.
- * K % 16 == 0.
+ *                   aligned.  On return it holds, with R(b) = b rounded up
+ *                   to a multiple of 256 and parts back to back:
+ *                     X~q [M, K] int8 at 0;
+ *                     the row steps dx [M] fp32 at R(M K);
+ *                     the column maxima of |x| [K] fp32, R(4 M) further;
+ *                     the column mask [K] fp32 (1 kept, 0 outlier), R(4 K)
+ *                     further; the O list [K] int32 (its first |O| entries,
+ *                     ascending), R(4 K) further; |O| int32, R(4 K) further.
+ * K % 16 == 0; K > 0 when M, N > 0.
  */
 size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K);
 int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
                          const float *w_scale, const void *w_f16, int64_t N,
                          float threshold, void *workspace,
                          size_t workspace_bytes, void *y, int y_dt,
-                         int32_t *n_outliers_out, void *stream);
+                         int32_t *acc_out, int32_t *n_outliers_out, void *stream);
 
 /*
  * Folding the smoothing into the norm that precedes the layer

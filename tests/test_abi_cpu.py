@@ -106,7 +106,7 @@ def test_mixed_validation():
 
     def call(thr=6.0, ws=FAKE, wsb=need, K=4096, x=FAKE):
         return L.sq_int8_mixed_matmul(x, 2048, K, FAKE, FAKE, FAKE, 4096, thr, ws, wsb, FAKE,
-                                      sq.SQ_F16, None, None)
+                                      sq.SQ_F16, None, None, None)
 
     assert call(thr=0.0) == ARG
     assert call(thr=-1.0) == ARG
@@ -116,6 +116,52 @@ def test_mixed_validation():
     assert call(ws=FAKE + 16) == ALIGN
     assert call(K=4100) == SHAPE
     assert call(x=None) == NULL
+
+
+def test_zero_length_rows_are_rejected_before_any_pointer_is_used():
+    """K == 0 with at least one row (or output): every entry point returns
+    SQ_ERR_SHAPE with NULL operands, so no kernel ever sees a row of no
+    elements (whose clamped tail loads would point before the buffer)."""
+    L = sq.lib()
+    for dt in (sq.SQ_F32, sq.SQ_F16, sq.SQ_BF16):
+        assert L.sq_smooth_weights(None, dt, 8, 0, None, None, FAKE, None) == SHAPE
+        assert L.sq_smooth_weights(None, dt, 8, 0, None, None, None, None) == SHAPE
+        assert L.sq_smooth_weights_folded(None, dt, 8, 0, None, None, None, FAKE, None) == SHAPE
+        assert L.sq_smooth_weights_fp8(None, dt, 8, 0, None, None, FAKE, None) == SHAPE
+        for mode in (sq.SQ_PER_TENSOR_STATIC, sq.SQ_PER_TOKEN_DYNAMIC):
+            assert L.sq_quantize_act(None, dt, 8, 0, None, mode, FAKE, None, FAKE, None) == SHAPE
+            assert L.sq_quantize_act_fp8(None, dt, 8, 0, None, mode, FAKE, None, FAKE,
+                                         None) == SHAPE
+    for ydt in (sq.SQ_F32, sq.SQ_F16, sq.SQ_BF16):
+        for M in (1, 8, 33, 300):   # decode and tiled launch shapes alike
+            assert L.sq_gemm_i8_dequant(None, None, M, 64, 0, FAKE, 1, FAKE, FAKE, ydt, None,
+                                        None) == SHAPE
+            assert L.sq_gemm_i8_dequant(None, None, M, 64, 0, None, 1, None, None, ydt, None,
+                                        None) == SHAPE
+        assert L.sq_gemm_fp8_dequant(None, None, 40, 64, 0, None, 1, None, None, ydt,
+                                     None) == SHAPE
+        assert L.sq_int8_mixed_matmul(None, 40, 0, None, None, None, 64, 6.0, None, 0, None,
+                                      ydt, None, None, None) == SHAPE
+    assert L.sq_norm_quantize_act(None, sq.SQ_F16, 8, 0, 0, None, None, 1e-5, 1, None, None,
+                                  FAKE, None) == SHAPE
+    # no rows or no outputs: nothing to do, any K
+    assert L.sq_smooth_weights(None, sq.SQ_F16, 0, 0, None, None, None, None) == OK
+    assert L.sq_quantize_act(None, sq.SQ_F16, 0, 0, None, 1, None, None, None, None) == OK
+    assert L.sq_gemm_i8_dequant(None, None, 0, 64, 0, None, 1, None, None, sq.SQ_F16, None,
+                                None) == OK
+    assert L.sq_gemm_i8_dequant(None, None, 8, 0, 0, None, 1, None, None, sq.SQ_F16, None,
+                                None) == OK
+
+
+def test_binding_rejects_zero_width_tensors_on_the_host():
+    """Zero-width torch tensors have a null data pointer; the binding passes it
+    through and the library's K == 0 check raises before any launch."""
+    torch = pytest.importorskip("torch")
+    L = sq.lib()
+    z = torch.empty((5, 0), dtype=torch.float16)
+    assert z.data_ptr() == 0
+    assert L.sq_quantize_act(z.data_ptr(), sq.SQ_F16, 5, 0, None, 1, None, z.data_ptr(), FAKE,
+                             None) == SHAPE
 
 
 def test_binding_requires_gpu_tensors():

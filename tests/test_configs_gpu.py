@@ -147,10 +147,32 @@ def test_llm_int8_2048(torch):
     X, W = cfg["X"], cfg["W"]
     log("llm_int8_2048")
     wq, ws, wq_o, ws_o = _weights(torch, W, None)
-    y, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), 6.0, with_count=True)
+    M, K = X.shape
+    work = torch.full((sq.int8_mixed_matmul_workspace(M, K),), 0xA5, dtype=torch.uint8,
+                      device="cuda")
+    y, acc, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), 6.0,
+                                       workspace=work, with_count=True, with_acc=True)
     r = oracle.int8_mixed_matmul(X, wq_o, ws_o, W, 6.0)
     assert list(r["idx"]) == list(cfg["dims"])
     assert int(host(cnt, torch)[0]) == 6
+    # the intermediates of the decomposition ([INT8-expl] §2.2), from the
+    # workspace's documented layout: O, X~q, the row steps, the column
+    # maxima and mask, and the int32 sums of the int8 part
+    wb = host(work, torch)
+    off = sq.int8_mixed_workspace_parts(M, K)
+    n_o = int(wb[off["count"]:off["count"] + 4].view(np.int32)[0])
+    assert n_o == 6
+    assert_bits_equal(wb[off["idx"]:off["idx"] + 4 * n_o].view(np.int32), r["idx"], "O list")
+    assert_bits_equal(wb[off["xq"]:off["xq"] + M * K].view(np.int8).reshape(M, K), r["xq"],
+                      "X~q")
+    assert_bits_equal(wb[off["x_scale"]:off["x_scale"] + 4 * M].view(np.float32), r["x_scale"],
+                      "row steps")
+    assert_bits_equal(wb[off["colmax"]:off["colmax"] + 4 * K].view(np.float32),
+                      oracle.absmax_cols(X), "column maxima")
+    mask = np.ones(K, np.float32)
+    mask[r["idx"]] = 0.0
+    assert_bits_equal(wb[off["mask"]:off["mask"] + 4 * K].view(np.float32), mask, "column mask")
+    assert_bits_equal(host(acc, torch), r["acc"], "acc")
     assert_bits_equal(host(y, torch), r["y"], "y")
     print(f"\nllm_int8_2048 rel. error vs fp64: {_rel_err(r['y'], X, W):.5f}")
 

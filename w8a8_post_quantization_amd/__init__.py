@@ -49,7 +49,7 @@ SIGNATURES = {
     "sq_gemm_i8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P, _P]),
     "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64]),
     "sq_int8_mixed_matmul": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, ctypes.c_size_t,
-                                  _P, _I, _P, _P]),
+                                  _P, _I, _P, _P, _P]),
     "sq_fold_norm": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "sq_norm_quantize_act": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
     "sq_static_scale": (_I, [_P, _P, _I64, _F, _P, _P]),
@@ -235,9 +235,24 @@ def int8_mixed_matmul_workspace(M, K) -> int:
     return int(lib().sq_int8_mixed_matmul_workspace(M, K))
 
 
+def int8_mixed_workspace_parts(M, K):
+    """Byte offsets of the parts the workspace holds on return (include/sq.h):
+    xq [M,K] int8, x_scale [M], colmax [K], mask [K] fp32, idx [K] int32,
+    count int32."""
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    off = {"xq": 0}
+    off["x_scale"] = off["xq"] + r(M * K)
+    off["colmax"] = off["x_scale"] + r(4 * M)
+    off["mask"] = off["colmax"] + r(4 * K)
+    off["idx"] = off["mask"] + r(4 * K)
+    off["count"] = off["idx"] + r(4 * K)
+    return off
+
+
 def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, workspace=None,
-                      with_count=False, stream=None):
-    """a6: LLM.int8() y [M,N] (and |O| as a 1-element int32 tensor)."""
+                      with_count=False, with_acc=False, stream=None):
+    """a6: LLM.int8() y [M,N], then (if asked) acc int32 [M,N] and |O| as a
+    1-element int32 tensor: y, (y, cnt), (y, acc) or (y, acc, cnt)."""
     torch = _torch()
     _check(x, "x", (torch.float16,), 2)
     _check(wq, "wq", (torch.int8,), 2)
@@ -250,10 +265,12 @@ def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, work
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x.device)
     cnt = torch.zeros(1, dtype=torch.int32, device=x.device) if with_count else None
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if with_acc else None
     _call("sq_int8_mixed_matmul", x.data_ptr(), M, K, wq.data_ptr(), w_scale.data_ptr(),
           w_f16.data_ptr(), N, float(threshold), workspace.data_ptr(), workspace.numel(),
-          y.data_ptr(), _dt(y), _ptr(cnt), _stream(stream))
-    return (y, cnt) if with_count else y
+          y.data_ptr(), _dt(y), _ptr(acc), _ptr(cnt), _stream(stream))
+    out = (y,) + ((acc,) if with_acc else ()) + ((cnt,) if with_count else ())
+    return out if len(out) > 1 else y
 
 
 def fold_norm(gamma, s, beta=None, stream=None):

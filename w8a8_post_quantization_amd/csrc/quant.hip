@@ -457,6 +457,7 @@ void launch_quant_rows_fp8(const void *x, int dt, int64_t rows, int64_t K, const
         if (!dynamic) launch_copy_f32(static_scale, scale, stream);
         return;
     }
+    if (K <= 0) return;  // rejected by the C ABI: the kernels clamp to the last vector
     int8_t *qq = reinterpret_cast<int8_t *>(q);
     if (dt == F32) launch_dt_fp8<F32>(x, rows, K, mul, dynamic, static_scale, qq, scale, stream);
     else if (dt == F16) launch_dt_fp8<F16>(x, rows, K, mul, dynamic, static_scale, qq, scale, stream);
@@ -471,6 +472,7 @@ void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const flo
             launch_copy_f32(static_scale, scale, stream);
         return;
     }
+    if (K <= 0) return;  // rejected by the C ABI: the kernels clamp to the last vector
     if (dt == F32) launch_dt<F32>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
     else if (dt == F16) launch_dt<F16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
     else launch_dt<BF16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);

@@ -92,7 +92,8 @@ int sq_smooth_weights(const void *w, int dt, int64_t N, int64_t K, const float *
     if (!valid_dt(dt)) return SQ_ERR_DTYPE;
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
     if (N == 0) return SQ_OK;
-    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (K == 0) return SQ_ERR_SHAPE;  // rows of no elements are rejected
+    if (!w_scale || !w || !wq) return SQ_ERR_NULL;
     if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(w_scale, 4))
         return SQ_ERR_ALIGN;
     sq::launch_quant_rows(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream));
@@ -104,7 +105,8 @@ int sq_smooth_weights_folded(const void *w, int dt, int64_t N, int64_t K, const 
     if (!valid_dt(dt)) return SQ_ERR_DTYPE;
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
     if (N == 0) return SQ_OK;
-    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (K == 0) return SQ_ERR_SHAPE;  // rows of no elements are rejected
+    if (!w_scale || !w || !wq) return SQ_ERR_NULL;
     if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(row_mul, 4) ||
         !aligned(w_scale, 4))
         return SQ_ERR_ALIGN;
@@ -117,7 +119,8 @@ int sq_smooth_weights_fp8(const void *w, int dt, int64_t N, int64_t K, const flo
     if (!valid_dt(dt)) return SQ_ERR_DTYPE;
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
     if (N == 0) return SQ_OK;
-    if (!w_scale || (K > 0 && (!w || !wq))) return SQ_ERR_NULL;
+    if (K == 0) return SQ_ERR_SHAPE;  // rows of no elements are rejected
+    if (!w_scale || !w || !wq) return SQ_ERR_NULL;
     if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(s, 16) || !aligned(w_scale, 4))
         return SQ_ERR_ALIGN;
     sq::launch_quant_rows_fp8(w, dt, N, K, s, 1, nullptr, wq, w_scale, st(stream));
@@ -131,8 +134,9 @@ int sq_quantize_act_fp8(const void *x, int dt, int64_t M, int64_t K, const float
     if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
     if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;
+    if (M > 0 && K == 0) return SQ_ERR_SHAPE;  // rows of no elements are rejected
     if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
-    if (M > 0 && K > 0 && (!x || !xq)) return SQ_ERR_NULL;
+    if (M > 0 && (!x || !xq)) return SQ_ERR_NULL;
     if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(inv_s, 16) || !aligned(x_scale, 4) ||
         !aligned(static_scale, 4))
         return SQ_ERR_ALIGN;
@@ -158,8 +162,9 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *in
     if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 16 != 0) return SQ_ERR_SHAPE;
     if (M == 0 && mode == SQ_PER_TOKEN_DYNAMIC) return SQ_OK;  // no rows, no steps
+    if (M > 0 && K == 0) return SQ_ERR_SHAPE;  // rows of no elements are rejected
     if (!x_scale || (mode == SQ_PER_TENSOR_STATIC && !static_scale)) return SQ_ERR_NULL;
-    if (M > 0 && K > 0 && (!x || !xq)) return SQ_ERR_NULL;
+    if (M > 0 && (!x || !xq)) return SQ_ERR_NULL;
     if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(inv_s, 16) || !aligned(x_scale, 4) ||
         !aligned(static_scale, 4))
         return SQ_ERR_ALIGN;
@@ -176,7 +181,8 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
         return SQ_ERR_SHAPE;
     if (K > 133143) return SQ_ERR_UNSUPPORTED;  // 127*127*K must fit int32
     if (M == 0 || N == 0) return SQ_OK;
-    if (!x_scale || !w_scale || !y || (K > 0 && (!xq || !wq))) return SQ_ERR_NULL;
+    if (K == 0) return SQ_ERR_SHAPE;  // an empty inner dimension
+    if (!x_scale || !w_scale || !y || !xq || !wq) return SQ_ERR_NULL;
     if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
         !aligned(y, esize(y_dt)) || !aligned(acc_out, 4))
         return SQ_ERR_ALIGN;
@@ -248,19 +254,20 @@ size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K) {
 int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
                          const float *w_scale, const void *w_f16, int64_t N, float threshold,
                          void *workspace, size_t workspace_bytes, void *y, int y_dt,
-                         int32_t *n_outliers_out, void *stream) {
+                         int32_t *acc_out, int32_t *n_outliers_out, void *stream) {
     if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
         return SQ_ERR_SHAPE;
     if (K > 133143) return SQ_ERR_UNSUPPORTED;
     if (!(threshold > 0.0f)) return SQ_ERR_ARG;  // also rejects NaN
     if (M == 0 || N == 0) return SQ_OK;
+    if (K == 0) return SQ_ERR_SHAPE;  // an empty inner dimension
     if (!x || !wq || !w_scale || !w_f16 || !y) return SQ_ERR_NULL;
     const MixedWs L = mixed_layout(M, K);
     if (!workspace || workspace_bytes < L.total) return SQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
     if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(w_f16, 16) || !aligned(w_scale, 4) ||
-        !aligned(y, esize(y_dt)) || !aligned(n_outliers_out, 4))
+        !aligned(y, esize(y_dt)) || !aligned(acc_out, 4) || !aligned(n_outliers_out, 4))
         return SQ_ERR_ALIGN;
     char *ws = static_cast<char *>(workspace);
     auto *xq = reinterpret_cast<int8_t *>(ws + L.xq);
@@ -274,7 +281,7 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
     sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
     sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
                       count};
-    sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, nullptr, &side, s);
+    sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, acc_out, &side, s);
     return finish();
 }
 
