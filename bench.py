@@ -1,24 +1,29 @@
 """Benchmark of the W8A8 SmoothQuant linear-layer path on one MI355X.
 
-A step is one pass of the whole SmoothQuant path over one batch of the
-30B-class prefill layer (X fp16 [256, 7168] with 6 outlier channels x
+A step is one per-call pass of the SmoothQuant W8A8 linear layer at the
+30B-class prefill shape (X fp16 [256, 7168] with 6 outlier channels x
 U(20,100), W fp16 [28672, 7168] ~ N(0, 0.025), alpha = 0.5, per-token int8 X,
 per-output-channel int8 W, bf16 out):
 
-  a1 abs-max of X   a1 abs-max of W   a2 smoothing factors
-  a3 W*s -> int8    a4 X/s -> int8    a5 int8 GEMM + dequant
+  a4  X * (1/s) -> int8 per token      a5  int8 GEMM + c_x (x) c_w dequant
+
+with the weights cold: each step reads the next of three int8 weight copies
+(616 MB, more than twice the 256 MB last-level cache), as a layer's weights
+are when a model runs.  The offline steps (a1 abs-max of X and W, a2 the
+smoothing factors, a3 W * s -> int8) are timed separately under `kernels`.
 
 `value` is the step's int8 GEMM work (2*M*N*K ops) divided by the step time
-(TOPS), i.e. whole-path throughput.  The JSON line also carries the
-roofline of the step's dominant kernel, per-kernel times, and separately
-timed kernel-level figures: the prefill GEMM with cold weights (rotating
-copies larger than the 256 MB last-level cache), decode GEMMs at M = 1, 8,
-32 (HBM GB/s), activation quantization and abs-max on a 940 MB stream, the
-LLM.int8() mixed matmul, the hidden-1024 decoder GEMM set and the fused
-norm -> int8 quantizer (smoothing folded into the norm).  All inputs
-are seeded synthetic data, generated on the host and resident in HBM before
-any timed region.  `cpu_baseline` times the CPU oracle on a bounded slice
-of the same step on this host.
+(TOPS).  `roofline` is the prefill GEMM's (the step's dominant kernel)
+against the int8 MFMA peak, with its fractions of the MFMA rate this GPU
+reaches in a loop with no memory traffic and of the HBM-attainable ceiling
+min(peak, ops/bytes x 8 TB/s).  Kernel-level extras follow: the GEMM with
+warm weights, decode GEMMs at M = 1, 8, 32 (HBM GB/s), activation
+quantization and abs-max on a 940 MB stream, the LLM.int8() mixed matmul,
+the hidden-1024 decoder GEMM set and the fused norm -> int8 quantizer.  All
+inputs are seeded synthetic data, generated on the host and resident in HBM
+before any timed region.  `cpu_baseline` times the CPU oracle on the same
+per-call pass over a bounded slice of the output channels on this host, and
+the other workloads' GEMMs beside it.
 """
 from __future__ import annotations
 
@@ -63,9 +68,12 @@ def parse():
 # Measured HBM traffic of a kernel comes from rocprofv3 counter runs kept in
 # profiles/ (a fenced ```json block in the summary).  It is reported only
 # while the kernel's sources still hash to what the counters were taken on.
-TRAFFIC_FILES = {"a3_smooth_weights": "a3_smooth_weights_prefill_30b_traffic.md"}
+TRAFFIC_FILES = {"a3_smooth_weights": "a3_smooth_weights_prefill_30b_traffic.md",
+                 "a5_gemm": "a5_gemm_prefill_30b_traffic.md"}
 KERNEL_SOURCES = {"a3_smooth_weights": ["w8a8_post_quantization_amd/csrc/quant.hip",
-                                        "w8a8_post_quantization_amd/csrc/sq_device.h"]}
+                                        "w8a8_post_quantization_amd/csrc/sq_device.h"],
+                  "a5_gemm": ["w8a8_post_quantization_amd/csrc/gemm.hip",
+                              "w8a8_post_quantization_amd/csrc/sq_device.h"]}
 
 
 def sources_sha256(kernel):
@@ -229,7 +237,7 @@ def main():
         if rc != 0:
             raise RuntimeError(f"{what}: {L.sq_status_str(rc).decode()}")
 
-    # ------------------------------------------------------------ the step
+    # ------------------------------------------------------------ inputs
     M, N, K = 256, 28672, 7168
     cfg = synth.prefill_30b(M, N, K)
     X, W = T(cfg["X"]), T(cfg["W"])
@@ -237,25 +245,37 @@ def main():
     f32 = dict(dtype=torch.float32, device=dev)
     xamax, wamax = torch.empty(K, **f32), torch.empty(K, **f32)
     s, inv_s = torch.empty(K, **f32), torch.empty(K, **f32)
-    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    NCOPY = 3  # 3 x 205 MB of int8 weights: beyond the 256 MB last-level cache
+    wqs = [torch.empty((N, K), dtype=torch.int8, device=dev) for _ in range(NCOPY)]
     ws = torch.empty(N, **f32)
     xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     xs = torch.empty(M, **f32)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     P = lambda t: t.data_ptr()  # noqa: E731
 
-    kernels = [
+    # The offline part of the layer (calibration statistics, smoothing
+    # factors, weight quantization): timed per kernel, not part of a step.
+    offline = [
         ("a1_absmax_x", lambda: chk(L.sq_absmax_reduce(P(X), 1, M, K, 0, P(xamax), sp), "a1x")),
         ("a1_absmax_w", lambda: chk(L.sq_absmax_reduce(P(W), 1, N, K, 0, P(wamax), sp), "a1w")),
         ("a2_scales", lambda: chk(L.sq_compute_scales(P(xamax), P(wamax), K, 0.5, P(s), P(inv_s),
                                                       None, sp), "a2")),
-        ("a3_smooth_weights", lambda: chk(L.sq_smooth_weights(P(W), 1, N, K, P(s), P(wq), P(ws),
-                                                              sp), "a3")),
-        ("a4_quantize_act", lambda: chk(L.sq_quantize_act(P(X), 1, M, K, P(inv_s), 1, None, P(xq),
-                                                          P(xs), sp), "a4")),
-        ("a5_gemm", lambda: chk(L.sq_gemm_i8_dequant(P(xq), P(wq), M, N, K, P(xs), 1, P(ws), P(y),
-                                                     2, None, sp), "a5")),
+        ("a3_smooth_weights", lambda: chk(L.sq_smooth_weights(P(W), 1, N, K, P(s), P(wqs[0]),
+                                                              P(ws), sp), "a3")),
     ]
+    for _, fn in offline:
+        fn()
+    for c in range(1, NCOPY):  # the same quantized weights in distinct memory
+        chk(L.sq_smooth_weights(P(W), 1, N, K, P(s), P(wqs[c]), P(ws), sp), "a3")
+    torch.cuda.synchronize()
+
+    def a4():
+        chk(L.sq_quantize_act(P(X), 1, M, K, P(inv_s), 1, None, P(xq), P(xs), sp), "a4")
+
+    def a5(i):
+        chk(L.sq_gemm_i8_dequant(P(xq), P(wqs[i % NCOPY]), M, N, K, P(xs), 1, P(ws), P(y), 2,
+                                 None, sp), "a5")
+
     bytes_per_call = {  # algorithmic HBM bytes of one launch
         "a1_absmax_x": M * K * 2 + 4 * K,
         "a1_absmax_w": N * K * 2 + 4 * K,
@@ -271,56 +291,58 @@ def main():
     n_warm = 0
     t_warm = time.perf_counter()
     while n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
-        for _, fn in kernels:
-            fn()
+        a4()
+        a5(n_warm)
         n_warm += 1
         if n_warm % 32 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    # Per-kernel breakdown, in a pass of its own (an event pair around every
-    # launch adds gaps between kernels).
+    # Per-kernel breakdown, in passes of their own (an event pair around every
+    # launch adds gaps between kernels): the step's two kernels, then the
+    # offline ones (a3 writes the first weight copy again, same bits).
     tm = Timer(torch)
-    for _ in range(args.steps):
-        for name, fn in kernels:
+    for i in range(args.steps):
+        tm.run("a4_quantize_act", a4)
+        tm.run("a5_gemm", lambda: a5(i))
+    for _ in range(max(3, args.steps // 4)):
+        for name, fn in offline:
             tm.run(name, fn)
     torch.cuda.synchronize()
     per_kernel = {}
-    for name, _ in kernels:
+    for name in ("a1_absmax_x", "a1_absmax_w", "a2_scales", "a3_smooth_weights",
+                 "a4_quantize_act", "a5_gemm"):
         us = tm.avg_us(name)
         per_kernel[name] = {"us": round(us, 2),
-                            "GBs": round(bytes_per_call[name] / us / 1e3, 1)}
+                            "GBs": round(bytes_per_call[name] / us / 1e3, 1),
+                            "offline": name not in ("a4_quantize_act", "a5_gemm")}
     per_kernel["a5_gemm"]["TOPS"] = round(gemm_ops / per_kernel["a5_gemm"]["us"] / 1e6, 1)
-    dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
 
-    # Timed steps: events only around the dominant kernel (its live duration
-    # for the roofline) and around the whole run.
+    # Timed steps: events around the whole run, and around each GEMM launch
+    # (its live duration, on the stream it runs on, for the roofline).
     live = Timer(torch)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
-        for name, fn in kernels:
-            if name == dom:
-                live.run(name, fn)
-            else:
-                fn()
+    for i in range(args.steps):
+        a4()
+        live.run("a5_gemm", lambda: a5(i))
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    dom_us = live.avg_us(dom)
-    if dom == "a5_gemm":
-        roof = {"bound": "mfma", "achieved": round(gemm_ops / dom_us / 1e6, 1),
-                "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(bytes_per_call[dom] / dom_us / 1e3, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dom
-    roof["kernel_us"] = round(dom_us, 2)
-    roof["traffic"] = measured_traffic(dom)
+    dom_us = live.avg_us("a5_gemm")
+    achieved = gemm_ops / dom_us / 1e6
+    attainable = min(PEAK_INT8_TOPS, gemm_ops / bytes_per_call["a5_gemm"] * PEAK_HBM_GBS / 1e3)
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": measured_traffic("a5_gemm"),
+            "kernel": "a5_gemm (gemm_pp 256x128 tiles, int8 MFMA 32x32x32)",
+            "kernel_us": round(dom_us, 2), "ops_per_launch": gemm_ops,
+            "algorithmic_bytes_per_launch": bytes_per_call["a5_gemm"],
+            "hbm_attainable": round(attainable, 1),
+            "frac_attainable": round(achieved / attainable, 4)}
     value = gemm_ops / (ms_per_step * 1e-3) / 1e12
 
     out = {
@@ -329,16 +351,20 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic (seeded SplitMix64 normals with planted outlier channels)",
-        "config": {"workload": "prefill_30b: SmoothQuant W8A8 linear layer, one full "
-                               "a1-a5 pass", "M": M, "N": N, "K": K, "alpha": 0.5,
+        "config": {"workload": "prefill_30b: SmoothQuant W8A8 linear layer per call "
+                               "(a4 quantize + a5 GEMM, weights cold: 3 rotating copies)",
+                   "M": M, "N": N, "K": K, "alpha": 0.5,
                    "x": "fp16, 6 channels x U(20,100)", "w": "fp16 N(0,0.025)",
                    "act_quant": "per-token dynamic", "y": "bf16"},
         "roofline": roof, "kernels": per_kernel, "wall_s_timed": round(wall, 3),
     }
-    del X, W
+    del X, W, wqs
 
     if not args.no_extras:
         out["extras"] = extras(torch, L, sp, T, chk)
+        mp = out["extras"].get("measured_peaks", {}).get("int8_mfma")
+        if mp:
+            roof["frac_measured_mfma"] = round(achieved / mp["rate"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -642,10 +668,14 @@ def extras(torch, L, _sp, T, chk):
 
 
 def cpu_baseline(seconds):
-    """The CPU oracle on a bounded slice of the step: the same a1-a5 pass over
-    all 256 tokens and K = 7168 but only the first n_cols output channels,
-    with n_cols sized for about `seconds` of work.  Reported in TOPS of the
-    slice's GEMM work over the slice's whole time."""
+    """The CPU oracle on this host.  The step's per-call pass (a4 quantize,
+    a5 GEMM) over all 256 tokens and K = 7168 but only the first n output
+    channels, n sized for about `seconds` of work on all host threads, and
+    again on one thread (about a quarter of that); reported in TOPS of the
+    slice's GEMM work over the slice's time.  Beside it, on all threads, the
+    other workloads at full shape: the hidden-1024 decoder GEMM set
+    (M = 4096, 7 GEMMs), decode (M = 32, N = 28672, K = 8192) and LLM.int8()
+    (2048 x 4096 x 4096, threshold 6)."""
     import oracle
     import synth
 
@@ -654,27 +684,62 @@ def cpu_baseline(seconds):
 
     def run(ncols):
         X, W, _ = synth.linear_layer(2, M, ncols, K, 6, 20.0, 100.0, 0.025)
-        t0 = time.perf_counter()
         xa = oracle.absmax_cols(X)
         wa = oracle.absmax_cols(W)
         s_, inv_ = oracle.compute_scales(xa, wa, 0.5)
         wq_, ws_ = oracle.smooth_weights(W, s_)
+        t0 = time.perf_counter()
         xq_, xs_ = oracle.quantize_act(X, inv_, oracle.PER_TOKEN_DYNAMIC)
         oracle.gemm_i8_dequant(xq_, wq_, xs_, ws_, y_dt=oracle.BF16, want_acc=False)
         return time.perf_counter() - t0
 
-    n = 64
+    n = 256
     t = run(n)
-    n = int(max(64, min(28672, n * seconds / max(t, 1e-3))))
+    n = int(max(256, min(28672, n * seconds / max(t, 1e-3))))
     t = run(n)
     ops = 2.0 * M * n * K
-    # the same pass on one thread, on a slice sized for about a quarter of the time
     oracle.set_num_threads(1)
     n1 = 64
     t1 = run(n1)
     n1 = int(max(64, min(28672, n1 * seconds / 4 / max(t1, 1e-3))))
     t1 = run(n1)
     oracle.set_num_threads(0)
+
+    rng = np.random.default_rng(0)
+    others = {}
+
+    def gemm_time(Mg, Ng, Kg, ydt):
+        xq_ = rng.integers(-127, 128, (Mg, Kg), dtype=np.int8)
+        wq_ = rng.integers(-127, 128, (Ng, Kg), dtype=np.int8)
+        xs_ = rng.uniform(1e-3, 1e-2, Mg).astype(np.float32)
+        ws_ = rng.uniform(1e-4, 1e-3, Ng).astype(np.float32)
+        t0 = time.perf_counter()
+        oracle.gemm_i8_dequant(xq_, wq_, xs_, ws_, y_dt=ydt, want_acc=False)
+        return time.perf_counter() - t0
+
+    tot_t, tot_ops = 0.0, 0.0
+    for _, ng, kg in synth.DECODER_1024_WEIGHTS:   # 256 of the 4096 token rows
+        tot_t += gemm_time(256, ng, kg, oracle.F16)
+        tot_ops += 2.0 * 256 * ng * kg
+    others["decoder_1024"] = {"s": round(tot_t, 2), "TOPS": round(tot_ops / tot_t / 1e12, 6),
+                              "sample": "the 7 GEMMs on 256 of the 4096 token rows"}
+    td = gemm_time(32, 28672, 8192, oracle.F16)
+    others["decode_8192_M32"] = {"s": round(td, 2),
+                                 "GBs": round(28672 * 8192 / td / 1e9, 3), "sample": "full"}
+    cfg = synth.llm_int8_2048()
+    Xm, Wm = cfg["X"], cfg["W"]
+    wq_, ws_ = oracle.smooth_weights(Wm, None)
+    rows = np.repeat(np.arange(0, 2048, 32), 4096)
+    cols = np.tile(np.arange(4096), 64)
+    t0 = time.perf_counter()
+    idx, xq_, xs_ = oracle.int8_mixed_prep(Xm, 6.0)
+    oracle.int8_mixed_at(Xm, xq_, xs_, wq_, ws_, Wm, idx, rows, cols)
+    tm_ = time.perf_counter() - t0
+    others["llm_int8_2048"] = {"s": round(tm_, 2),
+                               "TOPS": round(2.0 * rows.size * 4096 / tm_ / 1e12, 6),
+                               "sample": "outlier detection and X~ quantization in full, then "
+                                         "64 of the 2048 output rows"}
+
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -683,11 +748,12 @@ def cpu_baseline(seconds):
         pass
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "cpu": model,
-            "sample": f"full a1-a5 pass on X [256,7168] and the first {n} of 28672 output "
-                      f"channels of W ({t:.1f} s)",
+            "sample": f"per-call pass (a4 quantize + a5 GEMM) on X [256,7168] and the first {n} "
+                      f"of 28672 output channels of W ({t:.1f} s)",
             "one_thread": {"value": round(2.0 * M * n1 * K / t1 / 1e12, 6), "unit": "TOPS",
                            "sample": f"the same pass over the first {n1} output channels "
-                                     f"({t1:.1f} s)"}}
+                                     f"({t1:.1f} s)"},
+            "other_workloads_all_threads": others}
 
 
 if __name__ == "__main__":
