@@ -259,6 +259,28 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
                          int32_t *acc_out, int32_t *n_outliers_out, void *stream);
 
 /*
+ * sq_int8_mixed_matmul for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, arguments and results, with no
+ * workspace argument.  The decomposition's intermediates live in a device
+ * array of SQ_MIXED_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the call allocates nothing.
+ *   Returns SQ_ERR_WORKSPACE when sq_int8_mixed_matmul_workspace(M, K)
+ *   exceeds SQ_MIXED_SCRATCH_BYTES (e.g. M x K above ~33.5 M elements),
+ *   SQ_ERR_HIP when the array's device address cannot be obtained (looked up
+ *   once per GPU, with that GPU current, on the first call there).
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the
+ * caller.  The array keeps the last call's intermediates (laid out as the
+ * workspace above); each call rewrites everything it reads.
+ */
+#define SQ_MIXED_SCRATCH_BYTES (32u << 20)
+int sq_int8_mixed_matmul_noalloc(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                                 const float *w_scale, const void *w_f16, int64_t N,
+                                 float threshold, void *y, int y_dt, int32_t *acc_out,
+                                 int32_t *n_outliers_out, void *stream);
+
+/*
  * Folding the smoothing into the norm that precedes the layer
  * ([SQ-tutorial] section 融入 LayerNorm: the norm's output times 1/s_j is
  * obtained by dividing its parameters once).

@@ -18,7 +18,7 @@ FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced on these p
 def test_exports_every_declared_symbol():
     L = sq.lib()
     declared = sq.header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(L, name), name
         assert name in sq.SIGNATURES, name
@@ -116,6 +116,37 @@ def test_mixed_validation():
     assert call(ws=FAKE + 16) == ALIGN
     assert call(K=4100) == SHAPE
     assert call(x=None) == NULL
+
+
+def test_mixed_noalloc_validation():
+    """The allocation-free LLM.int8() entry point checks its arguments as the
+    workspace form does, and rejects shapes whose intermediates exceed its
+    per-GPU array, all on the host (no device call on these paths)."""
+    L = sq.lib()
+    f = L.sq_int8_mixed_matmul_noalloc
+    cap = 32 << 20   # SQ_MIXED_SCRATCH_BYTES
+
+    def call(M=2048, K=4096, N=4096, thr=6.0, x=FAKE, y=FAKE, ydt=sq.SQ_F16, acc=None):
+        return f(x, M, K, FAKE, FAKE, FAKE, N, thr, y, ydt, acc, None, None)
+
+    assert call(thr=0.0) == ARG
+    assert call(thr=float("nan")) == ARG
+    assert call(K=4100) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(x=None) == NULL
+    assert call(y=FAKE + 1) == ALIGN
+    assert call(acc=FAKE + 2) == ALIGN
+    assert call(ydt=7) == DTYPE
+    assert call(M=0, x=None, y=None) == OK
+    assert call(M=8192, K=8192) == WORKSPACE              # 64 MiB of int8 rows alone
+    # the largest M for K = 4096 that fits, and one row more
+    M = 1
+    while L.sq_int8_mixed_matmul_workspace(M + 1, 4096) <= cap:
+        M += 1
+    assert L.sq_int8_mixed_matmul_workspace(M, 4096) <= cap < \
+        L.sq_int8_mixed_matmul_workspace(M + 1, 4096)
+    assert call(M=M + 1, K=4096) == WORKSPACE
+    assert M >= 8000   # the 2048 x 4096 LLM.int8() workload fits with room
 
 
 def test_zero_length_rows_are_rejected_before_any_pointer_is_used():

@@ -50,6 +50,8 @@ SIGNATURES = {
     "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64]),
     "sq_int8_mixed_matmul": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, ctypes.c_size_t,
                                   _P, _I, _P, _P, _P]),
+    "sq_int8_mixed_matmul_noalloc": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, _I, _P, _P,
+                                          _P]),
     "sq_fold_norm": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "sq_norm_quantize_act": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
     "sq_static_scale": (_I, [_P, _P, _I64, _F, _P, _P]),
@@ -271,6 +273,25 @@ def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, work
           y.data_ptr(), _dt(y), _ptr(acc), _ptr(cnt), _stream(stream))
     out = (y,) + ((acc,) if with_acc else ()) + ((cnt,) if with_count else ())
     return out if len(out) > 1 else y
+
+
+def int8_mixed_matmul_noalloc(x, wq, w_scale, w_f16, threshold=6.0, out=None, acc=None,
+                              count=None, stream=None):
+    """a6 without a workspace (the library's per-GPU array): writes y into
+    `out` (required, [M,N]), and acc / |O| into `acc` / `count` when given.
+    Allocates nothing."""
+    torch = _torch()
+    _check(x, "x", (torch.float16,), 2)
+    _check(wq, "wq", (torch.int8,), 2)
+    _check(w_scale, "w_scale", (torch.float32,), 1)
+    _check(w_f16, "w_f16", (torch.float16,), 2)
+    _check(out, "out", (torch.float32, torch.float16, torch.bfloat16), 2)
+    M, K = x.shape
+    N = wq.shape[0]
+    _call("sq_int8_mixed_matmul_noalloc", x.data_ptr(), M, K, wq.data_ptr(), w_scale.data_ptr(),
+          w_f16.data_ptr(), N, float(threshold), out.data_ptr(), _dt(out), _ptr(acc), _ptr(count),
+          _stream(stream))
+    return out
 
 
 def fold_norm(gamma, s, beta=None, stream=None):

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "sq_launch.h"
 
@@ -27,6 +28,36 @@ inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 struct MixedWs {
     size_t xq, xs, colmax, mask, idx, count, total;
 };
+
+// Device memory for sq_int8_mixed_matmul_noalloc: one array per GPU, held
+// until the process ends.  Its name is a host-side stand-in for the device
+// symbol: host code uses only the per-device address that
+// hipGetSymbolAddress returns for it (scratch_ptr below).
+static __device__ __align__(256) char scratch[SQ_MIXED_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices];  // per-device address of `scratch`, once looked up
+
+// The current device's address of `scratch` (looked up once per device with
+// that device current), or null with *err set on failure.
+void *scratch_ptr(int *err) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = SQ_ERR_HIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            *err = SQ_ERR_HIP;
+            return nullptr;
+        }
+        scratch_dev[dev] = ptr;
+    }
+    return scratch_dev[dev];
+}
 
 MixedWs mixed_layout(int64_t M, int64_t K) {
     MixedWs w{};
@@ -251,38 +282,85 @@ size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K) {
     return mixed_layout(M, K).total;
 }
 
-int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
-                         const float *w_scale, const void *w_f16, int64_t N, float threshold,
-                         void *workspace, size_t workspace_bytes, void *y, int y_dt,
-                         int32_t *acc_out, int32_t *n_outliers_out, void *stream) {
-    if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
-    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
-        return SQ_ERR_SHAPE;
-    if (K > 133143) return SQ_ERR_UNSUPPORTED;
-    if (!(threshold > 0.0f)) return SQ_ERR_ARG;  // also rejects NaN
-    if (M == 0 || N == 0) return SQ_OK;
-    if (K == 0) return SQ_ERR_SHAPE;  // an empty inner dimension
-    if (!x || !wq || !w_scale || !w_f16 || !y) return SQ_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Arguments checked except the workspace; runs the three steps of the
+// decomposition with their buffers in `ws` (laid out by mixed_layout).
+int mixed_checked(const void *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
+                  const void *w_f16, int64_t N, float threshold, char *ws, void *y, int y_dt,
+                  int32_t *acc_out, int32_t *n_outliers_out, hipStream_t s) {
     const MixedWs L = mixed_layout(M, K);
-    if (!workspace || workspace_bytes < L.total) return SQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
-    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(w_f16, 16) || !aligned(w_scale, 4) ||
-        !aligned(y, esize(y_dt)) || !aligned(acc_out, 4) || !aligned(n_outliers_out, 4))
-        return SQ_ERR_ALIGN;
-    char *ws = static_cast<char *>(workspace);
     auto *xq = reinterpret_cast<int8_t *>(ws + L.xq);
     auto *xs = reinterpret_cast<float *>(ws + L.xs);
     auto *colmax = reinterpret_cast<float *>(ws + L.colmax);
     auto *mask = reinterpret_cast<float *>(ws + L.mask);
     auto *idx = reinterpret_cast<int32_t *>(ws + L.idx);
     auto *count = reinterpret_cast<int32_t *>(ws + L.count);
-    hipStream_t s = st(stream);
     sq::launch_outlier_prep(x, M, K, threshold, colmax, mask, idx, count, n_outliers_out, s);
     sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
     sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
                       count};
     sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, acc_out, &side, s);
     return finish();
+}
+
+// The checks both LLM.int8() entry points share (all but the workspace).
+int mixed_args(const void *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
+               const void *w_f16, int64_t N, float threshold, void *y, int y_dt,
+               int32_t *acc_out, int32_t *n_outliers_out, bool *nothing) {
+    *nothing = false;
+    if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
+        return SQ_ERR_SHAPE;
+    if (K > 133143) return SQ_ERR_UNSUPPORTED;
+    if (!(threshold > 0.0f)) return SQ_ERR_ARG;  // also rejects NaN
+    if (M == 0 || N == 0) {
+        *nothing = true;
+        return SQ_OK;
+    }
+    if (K == 0) return SQ_ERR_SHAPE;  // an empty inner dimension
+    if (!x || !wq || !w_scale || !w_f16 || !y) return SQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(w_f16, 16) || !aligned(w_scale, 4) ||
+        !aligned(y, esize(y_dt)) || !aligned(acc_out, 4) || !aligned(n_outliers_out, 4))
+        return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                         const float *w_scale, const void *w_f16, int64_t N, float threshold,
+                         void *workspace, size_t workspace_bytes, void *y, int y_dt,
+                         int32_t *acc_out, int32_t *n_outliers_out, void *stream) {
+    bool nothing = false;
+    int st_ = mixed_args(x, M, K, wq, w_scale, w_f16, N, threshold, y, y_dt, acc_out,
+                         n_outliers_out, &nothing);
+    if (st_ != SQ_OK || nothing) return st_;
+    if (!workspace || workspace_bytes < mixed_layout(M, K).total) return SQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
+    return mixed_checked(x, M, K, wq, w_scale, w_f16, N, threshold,
+                         static_cast<char *>(workspace), y, y_dt, acc_out, n_outliers_out,
+                         st(stream));
+}
+
+int sq_int8_mixed_matmul_noalloc(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                                 const float *w_scale, const void *w_f16, int64_t N,
+                                 float threshold, void *y, int y_dt, int32_t *acc_out,
+                                 int32_t *n_outliers_out, void *stream) {
+    bool nothing = false;
+    int st_ = mixed_args(x, M, K, wq, w_scale, w_f16, N, threshold, y, y_dt, acc_out,
+                         n_outliers_out, &nothing);
+    if (st_ != SQ_OK || nothing) return st_;
+    if (mixed_layout(M, K).total > (size_t)SQ_MIXED_SCRATCH_BYTES) return SQ_ERR_WORKSPACE;
+    int err = SQ_OK;
+    void *ws = scratch_ptr(&err);
+    if (!ws) return err;
+    return mixed_checked(x, M, K, wq, w_scale, w_f16, N, threshold, static_cast<char *>(ws), y,
+                         y_dt, acc_out, n_outliers_out, st(stream));
 }
 
 }  // extern "C"
