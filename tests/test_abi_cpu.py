@@ -23,6 +23,24 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name), name
         assert name in sq.SIGNATURES, name
     assert L.sq_version() == 103
+    test_only = sq.header_functions(sq.TEST_HEADER)
+    assert test_only == ["sq_gemm_fp8_dequant_tile", "sq_gemm_i8_dequant_tile",
+                         "sq_int8_mixed_matmul_tile"]
+    for name in test_only:
+        assert hasattr(L, name) and name in sq.SIGNATURES, name
+
+
+def test_forced_tile_is_checked():
+    L = sq.lib()
+    for bad in (-2, 3, 99):
+        assert L.sq_gemm_i8_dequant_tile(FAKE, FAKE, 64, 64, 128, FAKE, 1, FAKE, FAKE,
+                                         sq.SQ_F32, None, None, bad) == ARG
+        assert L.sq_gemm_fp8_dequant_tile(FAKE, FAKE, 64, 64, 128, FAKE, 1, FAKE, FAKE,
+                                          sq.SQ_F32, None, bad) == ARG
+        assert L.sq_int8_mixed_matmul_tile(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 6.0, FAKE, 1 << 20,
+                                           FAKE, sq.SQ_F16, None, None, None, bad) == ARG
+    assert L.sq_gemm_i8_dequant_tile(FAKE, FAKE, 64, 64, 40, FAKE, 1, FAKE, FAKE, sq.SQ_F32,
+                                     None, None, 1) == SHAPE
 
 
 def test_status_strings():

@@ -23,7 +23,6 @@ products' roundings and the output's:
     |y - fl(fl32(exact) * c)| <= |c| (that bound) + (2^-22 + u_out) |y_ref|
 with u_out the output's half ulp (0, 2^-11, 2^-8 for fp32, fp16, bf16).
 """
-import os
 
 import numpy as np
 import pytest
@@ -197,16 +196,12 @@ def test_gemm_fp8_parity(torch, M, N, K, ydt, per_row, tile):
     xs = (rng.random(M if per_row else 1) * 0.02 + 1e-3).astype(np.float32)
     ws = (rng.random(N) * 0.002 + 1e-5).astype(np.float32)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[ydt]
-    if tile is not None:
-        os.environ["SQ_GEMM_TILE"] = tile
-    try:
-        log(f"gemm_fp8 M={M} N={N} K={K} y={ydt} per_row={per_row} tile={tile}")
-        y = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
-                                out_dtype=tdt)
-        y2 = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
-                                 out_dtype=tdt)
-    finally:
-        os.environ.pop("SQ_GEMM_TILE", None)
+    t = None if tile is None else int(tile)
+    log(f"gemm_fp8 M={M} N={N} K={K} y={ydt} per_row={per_row} tile={tile}")
+    y = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                            out_dtype=tdt, tile=t)
+    y2 = sq.gemm_fp8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                             out_dtype=tdt, tile=t)
     _, acc = oracle.gemm_fp8_dequant(xq, wq, xs, ws, y_dt=YDT[ydt], per_row=int(per_row))
     ab, bs = _bound_terms(xq, wq)
     worst = _check_gemm(host(y, torch), ydt, xs, ws, acc, ab, bs, per_row, K)

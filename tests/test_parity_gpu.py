@@ -7,7 +7,6 @@ dequantized outputs bit-exact; smoothing factors within 4 ulp (the GPU and
 libm `pow` may differ in the last bit); downstream steps are fed the
 oracle's scale tensors ("given identical scale tensors").
 """
-import os
 
 import numpy as np
 import pytest
@@ -165,17 +164,13 @@ def test_gemm_parity(torch, M, N, K, ydt, per_row, tile):
     xs = (rng.random(M if per_row else 1) * 0.05 + 1e-3).astype(np.float32)
     ws = (rng.random(N) * 0.002 + 1e-5).astype(np.float32)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[ydt]
-    if tile is not None:
-        os.environ["SQ_GEMM_TILE"] = tile
-    try:
-        log(f"gemm M={M} N={N} K={K} y={ydt} per_row={per_row} tile={tile}")
-        xs_d = dev(xs, torch)
-        y, acc = sq.gemm_i8_dequant(dev(xq, torch), dev(wq, torch), xs_d, dev(ws, torch),
-                                    out_dtype=tdt, with_acc=True)
-        y2 = sq.gemm_i8_dequant(dev(xq, torch), dev(wq, torch), xs_d, dev(ws, torch),
-                                out_dtype=tdt)
-    finally:
-        os.environ.pop("SQ_GEMM_TILE", None)
+    t = None if tile is None else int(tile)
+    log(f"gemm M={M} N={N} K={K} y={ydt} per_row={per_row} tile={tile}")
+    xs_d = dev(xs, torch)
+    y, acc = sq.gemm_i8_dequant(dev(xq, torch), dev(wq, torch), xs_d, dev(ws, torch),
+                                out_dtype=tdt, with_acc=True, tile=t)
+    y2 = sq.gemm_i8_dequant(dev(xq, torch), dev(wq, torch), xs_d, dev(ws, torch),
+                            out_dtype=tdt, tile=t)
     y_o, acc_o = oracle.gemm_i8_dequant(xq, wq, xs, ws, y_dt=YDT[ydt],
                                         per_row=int(per_row and M > 1))
     assert_bits_equal(host(acc, torch), acc_o, "acc")
@@ -221,13 +216,8 @@ def test_mixed_parity(torch, M, N, K, thr, tile, n_dims):
     log(f"mixed M={M} N={N} K={K} thr={thr} tile={tile} n_dims={n_dims}")
     wq, ws = sq.smooth_weights(dev(W, torch))
     assert_bits_equal(host(wq, torch), wq_o, "wq")
-    if tile is not None:
-        os.environ["SQ_GEMM_TILE"] = tile
-    try:
-        y, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), thr,
-                                      with_count=True)
-    finally:
-        os.environ.pop("SQ_GEMM_TILE", None)
+    y, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), thr, with_count=True,
+                                  tile=None if tile is None else int(tile))
     r = oracle.int8_mixed_matmul(X, wq_o, ws_o, W, thr)
     assert int(host(cnt, torch)[0]) == r["idx"].size
     assert_bits_equal(host(y, torch), r["y"], "y")

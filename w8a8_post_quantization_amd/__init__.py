@@ -26,6 +26,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sq.h")
+TEST_HEADER = os.path.join(os.path.dirname(HERE), "include", "sq_test.h")
 
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_PER_TENSOR_STATIC, SQ_PER_TOKEN_DYNAMIC = 0, 1
@@ -58,6 +59,11 @@ SIGNATURES = {
     "sq_smooth_weights_fp8": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P]),
     "sq_quantize_act_fp8": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "sq_gemm_fp8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P]),
+    # coverage entry points (include/sq_test.h): the tiled GEMM's block shape forced
+    "sq_gemm_i8_dequant_tile": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P, _P, _I]),
+    "sq_gemm_fp8_dequant_tile": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P, _I]),
+    "sq_int8_mixed_matmul_tile": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, ctypes.c_size_t,
+                                       _P, _I, _P, _P, _P, _I]),
 }
 
 
@@ -209,8 +215,9 @@ def quantize_act(x, inv_s=None, mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, ou
 
 
 def gemm_i8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, with_acc=False, out=None,
-                    stream=None):
-    """a5: y [M,N] (and acc int32 [M,N] if with_acc)."""
+                    stream=None, tile=None):
+    """a5: y [M,N] (and acc int32 [M,N] if with_acc).  tile 0 | 1 | 2 forces
+    the tiled kernel's block shape (include/sq_test.h; same bits)."""
     torch = _torch()
     _check(xq, "xq", (torch.int8,), 2)
     _check(wq, "wq", (torch.int8,), 2)
@@ -228,8 +235,13 @@ def gemm_i8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, with_acc=False, ou
     y = out if out is not None else torch.empty(
         (M, N), dtype=out_dtype or torch.float32, device=xq.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if with_acc else None
-    _call("sq_gemm_i8_dequant", xq.data_ptr(), wq.data_ptr(), M, N, K, x_scale.data_ptr(),
-          per_row, w_scale.data_ptr(), y.data_ptr(), _dt(y), _ptr(acc), _stream(stream))
+    if tile is None:
+        _call("sq_gemm_i8_dequant", xq.data_ptr(), wq.data_ptr(), M, N, K, x_scale.data_ptr(),
+              per_row, w_scale.data_ptr(), y.data_ptr(), _dt(y), _ptr(acc), _stream(stream))
+    else:
+        _call("sq_gemm_i8_dequant_tile", xq.data_ptr(), wq.data_ptr(), M, N, K,
+              x_scale.data_ptr(), per_row, w_scale.data_ptr(), y.data_ptr(), _dt(y), _ptr(acc),
+              _stream(stream), int(tile))
     return (y, acc) if with_acc else y
 
 
@@ -252,7 +264,7 @@ def int8_mixed_workspace_parts(M, K):
 
 
 def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, workspace=None,
-                      with_count=False, with_acc=False, stream=None):
+                      with_count=False, with_acc=False, stream=None, tile=None):
     """a6: LLM.int8() y [M,N], then (if asked) acc int32 [M,N] and |O| as a
     1-element int32 tensor: y, (y, cnt), (y, acc) or (y, acc, cnt)."""
     torch = _torch()
@@ -268,9 +280,13 @@ def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, work
     y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x.device)
     cnt = torch.zeros(1, dtype=torch.int32, device=x.device) if with_count else None
     acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if with_acc else None
-    _call("sq_int8_mixed_matmul", x.data_ptr(), M, K, wq.data_ptr(), w_scale.data_ptr(),
-          w_f16.data_ptr(), N, float(threshold), workspace.data_ptr(), workspace.numel(),
-          y.data_ptr(), _dt(y), _ptr(acc), _ptr(cnt), _stream(stream))
+    args = (x.data_ptr(), M, K, wq.data_ptr(), w_scale.data_ptr(), w_f16.data_ptr(), N,
+            float(threshold), workspace.data_ptr(), workspace.numel(), y.data_ptr(), _dt(y),
+            _ptr(acc), _ptr(cnt), _stream(stream))
+    if tile is None:
+        _call("sq_int8_mixed_matmul", *args)
+    else:
+        _call("sq_int8_mixed_matmul_tile", *args, int(tile))
     out = (y,) + ((acc,) if with_acc else ()) + ((cnt,) if with_count else ())
     return out if len(out) > 1 else y
 
@@ -379,7 +395,8 @@ def quantize_act_fp8(x, inv_s=None, mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None
     return xq, xs
 
 
-def gemm_fp8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, out=None, stream=None):
+def gemm_fp8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, out=None, stream=None,
+                     tile=None):
     """f4: y [M,N] = fl(acc * fl(x_scale * w_scale)) with acc the fp32 sum of
     the e4m3 products (K % 128 == 0)."""
     torch = _torch()
@@ -398,6 +415,11 @@ def gemm_fp8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, out=None, stream=
         raise ValueError(f"w_scale has {w_scale.numel()} elements for N = {N}")
     dt = out_dtype or torch.float16
     y = out if out is not None else torch.empty((M, N), dtype=dt, device=xq.device)
-    _call("sq_gemm_fp8_dequant", xq.data_ptr(), wq.data_ptr(), M, N, K, x_scale.data_ptr(),
-          int(per_row), w_scale.data_ptr(), y.data_ptr(), _dt(y), _stream(stream))
+    if tile is None:
+        _call("sq_gemm_fp8_dequant", xq.data_ptr(), wq.data_ptr(), M, N, K, x_scale.data_ptr(),
+              int(per_row), w_scale.data_ptr(), y.data_ptr(), _dt(y), _stream(stream))
+    else:
+        _call("sq_gemm_fp8_dequant_tile", xq.data_ptr(), wq.data_ptr(), M, N, K,
+              x_scale.data_ptr(), int(per_row), w_scale.data_ptr(), y.data_ptr(), _dt(y),
+              _stream(stream), int(tile))
     return y

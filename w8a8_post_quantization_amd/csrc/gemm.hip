@@ -24,8 +24,6 @@
 // An integer dot product does not depend on the order of its terms, so the
 // assignment of K bytes to MFMA lanes only has to be the same for both
 // operands; the float epilogue is per element and order-free.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "sq_device.h"
@@ -1182,7 +1180,7 @@ static int pick_tile(int64_t M, int64_t N, int64_t K) {
 
 void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
                  const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
-                 int32_t *acc_out, const SideTerm *side, hipStream_t stream) {
+                 int32_t *acc_out, const SideTerm *side, hipStream_t stream, int force_tile) {
     // K >= 16 past the C ABI's checks; every kernel below clamps its tail
     // loads to the last K stage or chunk, which must exist.
     if (M <= 0 || N <= 0 || K <= 0) return;
@@ -1190,11 +1188,8 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     a.xq = xq; a.wq = wq; a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.xs = x_scale; a.xs_per_row = per_row; a.ws = w_scale; a.y = y; a.acc_out = acc_out;
     const bool pipe = K % 128 == 0;
-    // SQ_GEMM_TILE=0|1|2 forces a tile shape (for coverage of every shape).
-    int tile = pick_tile(M, N, K);
-    if (const char *e = getenv("SQ_GEMM_TILE")) {
-        if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
-    }
+    // force_tile 0 | 1 | 2 (the coverage entry points) overrides the choice.
+    const int tile = force_tile >= 0 && force_tile <= 2 ? force_tile : pick_tile(M, N, K);
     if (side) {
         // With the side term 256 x 256 tiles would need the side sums next
         // to 128 accumulator registers: the 256-row choices take 256 x 128.
@@ -1238,7 +1233,7 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
 // pipelined one.
 void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
                      const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
-                     hipStream_t stream) {
+                     hipStream_t stream, int force_tile) {
     if (M <= 0 || N <= 0 || K <= 0) return;  // tail loads clamp to the last stage
     GemmArgs a{};
     a.xq = reinterpret_cast<const int8_t *>(xq);
@@ -1252,10 +1247,7 @@ void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
         else launch_dec_t<8, 2, 2, 2, true, true>(a, y_dt, stream);
         return;
     }
-    int tile = pick_tile(M, N, K);
-    if (const char *e = getenv("SQ_GEMM_TILE")) {
-        if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) tile = e[0] - '0';
-    }
+    const int tile = force_tile >= 0 && force_tile <= 2 ? force_tile : pick_tile(M, N, K);
     switch (tile) {
         case 0: launch_pipe_t<256, 256, 4, 2, 2, 2, false, true>(a, y_dt, stream); break;
         case 1: launch_pipe_t<256, 128, 4, 2, 3, 3, false, true>(a, y_dt, stream); break;

@@ -301,10 +301,11 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
     uint4 b0[ITS], b1[ITS];
     load_row(r_begin, b0);
     // The prefetch is conditional: no load is issued past the block's last
-    // row.  (An unconditional prefetch that re-read an already fetched row
-    // gave wrong sums on this GPU: that load hits in cache, and the exact
-    // wait counts the compiler derives for the other buffer assume every
-    // load retires in issue order.)
+    // row.  (A variant whose prefetch re-read the block's last row
+    // unconditionally gave wrong sums now and then; it was not kept and its
+    // cause was not found.  It was not the order in which loads return: a
+    // wave's vector-memory loads return in issue order, which the partial
+    // waits of every kernel here, and the compiler's own, rely on.)
     for (int64_t r = r_begin;; r += 2) {
         if (r + 1 < r_end) load_row(r + 1, b1);
         process(r, b0, std::integral_constant<int, 0>{});

@@ -2,6 +2,7 @@
 // then kernel launches on the caller's stream.  No allocation, no
 // synchronization, no state besides the kernels themselves.
 #include "../../include/sq.h"
+#include "../../include/sq_test.h"
 
 #include <hip/hip_runtime.h>
 
@@ -204,9 +205,10 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *in
     return finish();
 }
 
-int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
-                       const float *x_scale, int x_scale_per_row, const float *w_scale, void *y,
-                       int y_dt, int32_t *acc_out, void *stream) {
+int sq_gemm_i8_dequant_tile(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                            const float *x_scale, int x_scale_per_row, const float *w_scale,
+                            void *y, int y_dt, int32_t *acc_out, void *stream, int tile) {
+    if (tile < -1 || tile > 2) return SQ_ERR_ARG;
     if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
         return SQ_ERR_SHAPE;
@@ -218,13 +220,21 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N,
         !aligned(y, esize(y_dt)) || !aligned(acc_out, 4))
         return SQ_ERR_ALIGN;
     sq::launch_gemm(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
-                    acc_out, nullptr, st(stream));
+                    acc_out, nullptr, st(stream), tile);
     return finish();
 }
 
-int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
-                        const float *x_scale, int x_scale_per_row, const float *w_scale,
-                        void *y, int y_dt, void *stream) {
+int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                       const float *x_scale, int x_scale_per_row, const float *w_scale, void *y,
+                       int y_dt, int32_t *acc_out, void *stream) {
+    return sq_gemm_i8_dequant_tile(xq, wq, M, N, K, x_scale, x_scale_per_row, w_scale, y, y_dt,
+                                   acc_out, stream, -1);
+}
+
+int sq_gemm_fp8_dequant_tile(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
+                             int64_t K, const float *x_scale, int x_scale_per_row,
+                             const float *w_scale, void *y, int y_dt, void *stream, int tile) {
+    if (tile < -1 || tile > 2) return SQ_ERR_ARG;
     if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 128 != 0)
         return SQ_ERR_SHAPE;
@@ -235,8 +245,15 @@ int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t
         !aligned(y, esize(y_dt)))
         return SQ_ERR_ALIGN;
     sq::launch_gemm_fp8(xq, wq, M, N, K, x_scale, x_scale_per_row ? 1 : 0, w_scale, y, y_dt,
-                        st(stream));
+                        st(stream), tile);
     return finish();
+}
+
+int sq_gemm_fp8_dequant(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
+                        const float *x_scale, int x_scale_per_row, const float *w_scale,
+                        void *y, int y_dt, void *stream) {
+    return sq_gemm_fp8_dequant_tile(xq, wq, M, N, K, x_scale, x_scale_per_row, w_scale, y, y_dt,
+                                    stream, -1);
 }
 
 int sq_fold_norm(const float *gamma, const float *beta, const float *s, int64_t K,
@@ -290,7 +307,7 @@ namespace {
 // decomposition with their buffers in `ws` (laid out by mixed_layout).
 int mixed_checked(const void *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
                   const void *w_f16, int64_t N, float threshold, char *ws, void *y, int y_dt,
-                  int32_t *acc_out, int32_t *n_outliers_out, hipStream_t s) {
+                  int32_t *acc_out, int32_t *n_outliers_out, hipStream_t s, int tile) {
     const MixedWs L = mixed_layout(M, K);
     auto *xq = reinterpret_cast<int8_t *>(ws + L.xq);
     auto *xs = reinterpret_cast<float *>(ws + L.xs);
@@ -302,7 +319,7 @@ int mixed_checked(const void *x, int64_t M, int64_t K, const int8_t *wq, const f
     sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
     sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
                       count};
-    sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, acc_out, &side, s);
+    sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, acc_out, &side, s, tile);
     return finish();
 }
 
@@ -332,10 +349,12 @@ int mixed_args(const void *x, int64_t M, int64_t K, const int8_t *wq, const floa
 
 extern "C" {
 
-int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
-                         const float *w_scale, const void *w_f16, int64_t N, float threshold,
-                         void *workspace, size_t workspace_bytes, void *y, int y_dt,
-                         int32_t *acc_out, int32_t *n_outliers_out, void *stream) {
+int sq_int8_mixed_matmul_tile(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                              const float *w_scale, const void *w_f16, int64_t N,
+                              float threshold, void *workspace, size_t workspace_bytes, void *y,
+                              int y_dt, int32_t *acc_out, int32_t *n_outliers_out, void *stream,
+                              int tile) {
+    if (tile < -1 || tile > 2) return SQ_ERR_ARG;
     bool nothing = false;
     int st_ = mixed_args(x, M, K, wq, w_scale, w_f16, N, threshold, y, y_dt, acc_out,
                          n_outliers_out, &nothing);
@@ -344,7 +363,16 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
     if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
     return mixed_checked(x, M, K, wq, w_scale, w_f16, N, threshold,
                          static_cast<char *>(workspace), y, y_dt, acc_out, n_outliers_out,
-                         st(stream));
+                         st(stream), tile);
+}
+
+int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
+                         const float *w_scale, const void *w_f16, int64_t N, float threshold,
+                         void *workspace, size_t workspace_bytes, void *y, int y_dt,
+                         int32_t *acc_out, int32_t *n_outliers_out, void *stream) {
+    return sq_int8_mixed_matmul_tile(x, M, K, wq, w_scale, w_f16, N, threshold, workspace,
+                                     workspace_bytes, y, y_dt, acc_out, n_outliers_out, stream,
+                                     -1);
 }
 
 int sq_int8_mixed_matmul_noalloc(const void *x, int64_t M, int64_t K, const int8_t *wq,
@@ -360,7 +388,7 @@ int sq_int8_mixed_matmul_noalloc(const void *x, int64_t M, int64_t K, const int8
     void *ws = scratch_ptr(&err);
     if (!ws) return err;
     return mixed_checked(x, M, K, wq, w_scale, w_f16, N, threshold, static_cast<char *>(ws), y,
-                         y_dt, acc_out, n_outliers_out, st(stream));
+                         y_dt, acc_out, n_outliers_out, st(stream), -1);
 }
 
 }  // extern "C"

@@ -33,7 +33,7 @@ void launch_static_scale(const float *act_amax, const float *inv_s, int64_t K, f
 // e4m3 x e4m3 -> fp32 GEMM, y = fl(acc * fl(dx * dw)); K % 128 == 0.
 void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N, int64_t K,
                      const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
-                     hipStream_t stream);
+                     hipStream_t stream, int force_tile = -1);
 
 struct SideTerm {  // LLM.int8() fp16 side product over outlier columns
     const uint16_t *x16;   // [M, K]
@@ -42,9 +42,13 @@ struct SideTerm {  // LLM.int8() fp16 side product over outlier columns
     const int32_t *count;  // device |O|
 };
 
+// force_tile: -1 the launcher's choice; 0, 1, 2 the tiled kernels' block
+// shape 256 x 256, 256 x 128, 128 x 128 (M > 32; the coverage entry points
+// of sq_test.h), all giving the same bits.
 void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
                  const float *x_scale, int per_row, const float *w_scale, void *y, int y_dt,
-                 int32_t *acc_out, const SideTerm *side, hipStream_t stream);
+                 int32_t *acc_out, const SideTerm *side, hipStream_t stream,
+                 int force_tile = -1);
 
 // LLM.int8() preparation: column abs-max of x into colmax, then the mask
 // (1.0 keep / 0.0 outlier), the ascending O list and its count (also into
