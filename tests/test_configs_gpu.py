@@ -199,6 +199,17 @@ def test_activation_stream(torch):
     xq8_o, xs8_o = oracle.quantize_act_fp8(X, inv)
     assert_bits_equal(host(xs8, torch), xs8_o, "x_scale e4m3")
     assert_bits_equal(host(xq8, torch), xq8_o, "xq e4m3")
+    # the fused LayerNorm -> int8 (beta, per token) the benchmark times on
+    # this stream: 65536 rows, 32 per block, beta staged in LDS
+    log("stream fused norm -> int8")
+    g, b = synth.norm_params(X.shape[1])
+    xqn, xsn = sq.norm_quantize_act(dev(X, torch), dev(g, torch), dev(b, torch),
+                                    sq.SQ_NORM_LAYER, 1e-5, sq.SQ_PER_TOKEN_DYNAMIC)
+    xqn_o, xsn_o = oracle.norm_quantize(X, g, b, oracle.NORM_LAYER, 1e-5,
+                                        oracle.PER_TOKEN_DYNAMIC, None)
+    assert_bits_equal(host(xsn, torch), xsn_o, "x_scale (norm)")
+    assert_bits_equal(host(xqn, torch), xqn_o, "xq (norm)")
+    del xqn, xsn, xqn_o
     log("stream a4 e4m3 static")
     st8 = oracle.static_scale(oracle.absmax_cols(X), inv, 448.0)
     xq8, xs8 = sq.quantize_act_fp8(dev(X, torch), dev(inv, torch), sq.SQ_PER_TENSOR_STATIC,
