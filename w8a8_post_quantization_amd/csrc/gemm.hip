@@ -60,7 +60,28 @@ struct GemmArgs {
     const int32_t *idx;
     const int32_t *count;
     int tiles_n;
+    int tiles_m;
+    int xcd_gm, xcd_gn;  // XCD grid of the tile mapping (tile_of), or 0: row-major
 };
+
+// The tile of block b.  The hardware deals a kernel's blocks to the 8 XCDs
+// round-robin (block b to XCD b % 8), and each XCD has its own L2.  With an
+// XCD grid gm x gn (gm | tiles_m, gn | tiles_n, gm gn = 8) XCD x takes the
+// tiles of one sub-rectangle (tiles_m / gm) x (tiles_n / gn) of the tile
+// grid, row-major, so it fetches only those activation rows and weight rows
+// instead of most of both.  Any mapping gives the same results (a
+// bijection of tiles); only the cache traffic changes.
+__device__ __forceinline__ void tile_of(const GemmArgs &p, int b, int &tm, int &tn) {
+    if (p.xcd_gm == 0) {
+        tm = b / p.tiles_n;
+        tn = b % p.tiles_n;
+        return;
+    }
+    const int x = b & 7, j = b >> 3;
+    const int rm = p.tiles_m / p.xcd_gm, rn = p.tiles_n / p.xcd_gn;
+    tm = (x / p.xcd_gn) * rm + j / rn;
+    tn = (x % p.xcd_gn) * rn + j % rn;
+}
 
 // LDS layout of a staged chunk of outlier columns, column-major so that one
 // 16-byte read gives four consecutive rows of one column: activation values
@@ -248,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int tile_m = blockIdx.x / p.tiles_n, tile_n = blockIdx.x % p.tiles_n;
+    int tile_m, tile_n;
+    tile_of(p, blockIdx.x, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int M = p.M, N = p.N, K = p.K;
     TileScales<BM, BN> scl;
@@ -704,7 +726,8 @@ gemm_pp(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int tile_m = blockIdx.x / p.tiles_n, tile_n = blockIdx.x % p.tiles_n;
+    int tile_m, tile_n;
+    tile_of(p, blockIdx.x, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int M = p.M, N = p.N, K = p.K;
     TileScales<BM, BN> scl;
@@ -1117,10 +1140,30 @@ __global__ __launch_bounds__(256) void gemm_dec(GemmArgs p) {
 
 // ---------------------------------------------------------------- launch
 
+// XCD grid for tile_of: the factorization gm x gn = 8 (gm | tm, gn | tn)
+// that fetches the fewest operand bytes per XCD, rm BM + rn BN rows of K
+// bytes; none (row-major order) when the tiles do not split 8 ways.
+static void set_xcd_grid(GemmArgs &a, int tm, int tn, int bm, int bn) {
+    a.tiles_m = tm;
+    a.tiles_n = tn;
+    a.xcd_gm = a.xcd_gn = 0;
+    long best = -1;
+    for (int gm = 1; gm <= 8; gm *= 2) {
+        const int gn = 8 / gm;
+        if (tm % gm || tn % gn) continue;
+        const long cost = (long)(tm / gm) * bm + (long)(tn / gn) * bn;
+        if (best < 0 || cost < best) {
+            best = cost;
+            a.xcd_gm = gm;
+            a.xcd_gn = gn;
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, bool SIDE>
 static void launch_tile_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    a.tiles_n = tn;
+    set_xcd_grid(a, tm, tn, BM, BN);
     dim3 grid((unsigned)(tm * tn)), block(256);
     if (y_dt == F32) gemm_tile<BM, BN, WM, WN, F32, SIDE><<<grid, block, 0, stream>>>(a);
     else if (y_dt == F16) gemm_tile<BM, BN, WM, WN, F16, SIDE><<<grid, block, 0, stream>>>(a);
@@ -1130,7 +1173,7 @@ static void launch_tile_t(GemmArgs &a, int y_dt, hipStream_t stream) {
 template <int BM, int BN, int WM, int WN, int STA, int STB, bool SIDE, bool F8 = false>
 static void launch_pipe_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    a.tiles_n = tn;
+    set_xcd_grid(a, tm, tn, BM, BN);
     dim3 grid((unsigned)(tm * tn)), block(64 * WM * WN);
     if (y_dt == F32) gemm_pp<BM, BN, WM, WN, STA, STB, F32, SIDE, F8><<<grid, block, 0, stream>>>(a);
     else if (y_dt == F16) gemm_pp<BM, BN, WM, WN, STA, STB, F16, SIDE, F8><<<grid, block, 0, stream>>>(a);
