@@ -195,7 +195,7 @@ def profile_gemms():
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
     ws = torch.empty(N, dtype=torch.float32, device=dev)
     chk(L.sq_smooth_weights(P(w16), 1, N, K, None, P(wq), P(ws), sp), "llm_int8 weights")
-    need = L.sq_int8_mixed_matmul_workspace(M, K)
+    need = L.sq_int8_mixed_matmul_workspace(M, N, K)
     work = torch.empty(need, dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     for _ in range(3):
@@ -599,7 +599,7 @@ def extras(torch, L, _sp, T, chk):
     wq = torch.empty((N, K), dtype=torch.int8, device=dev)
     ws = torch.empty(N, dtype=torch.float32, device=dev)
     chk(L.sq_smooth_weights(P(Wm), 1, N, K, None, P(wq), P(ws), sp), "wq")
-    need = L.sq_int8_mixed_matmul_workspace(M, K)
+    need = L.sq_int8_mixed_matmul_workspace(M, N, K)
     wsp = torch.empty(need, dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)

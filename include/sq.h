@@ -240,18 +240,25 @@ int sq_gemm_i8_dequant(const int8_t *xq, const int8_t *wq, int64_t M,
  *   acc_out   [M, N] int32 out or NULL: the int8 sums acc (for checking).
  *   n_outliers_out  device int32 out or NULL: |O|.
  *   workspace       device memory of at least
- *                   sq_int8_mixed_matmul_workspace(M, K) bytes, 256-byte
+ *                   sq_int8_mixed_matmul_workspace(M, N, K) bytes, 256-byte
  *                   aligned.  On return it holds, with R(b) = b rounded up
- *                   to a multiple of 256 and parts back to back:
+ *                   to a multiple of 256, C = min(K, SQ_MIXED_SIDE_COLS)
+ *                   and parts back to back:
  *                     X~q [M, K] int8 at 0;
  *                     the row steps dx [M] fp32 at R(M K);
  *                     the column maxima of |x| [K] fp32, R(4 M) further;
  *                     the column mask [K] fp32 (1 kept, 0 outlier), R(4 K)
  *                     further; the O list [K] int32 (its first |O| entries,
- *                     ascending), R(4 K) further; |O| int32, R(4 K) further.
+ *                     ascending), R(4 K) further; |O| int32, R(4 K) further;
+ *                     when |O| <= C, the side operands as fp32, their first
+ *                     |O| rows: x[m, O_t] at [t, m] of a [C, M] array 256
+ *                     bytes further, w[n, O_t] at [t, n] of a [C, N] array
+ *                     R(4 C M) further (not written when |O| > C: the side
+ *                     product then reads x and w_f16 directly).
  * K % 16 == 0; K > 0 when M, N > 0.
  */
-size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K);
+#define SQ_MIXED_SIDE_COLS 128
+size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t N, int64_t K);
 int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
                          const float *w_scale, const void *w_f16, int64_t N,
                          float threshold, void *workspace,
@@ -265,8 +272,9 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
  * workspace argument.  The decomposition's intermediates live in a device
  * array of SQ_MIXED_SCRATCH_BYTES that the library holds on every GPU it
  * runs on until the process ends; the call allocates nothing.
- *   Returns SQ_ERR_WORKSPACE when sq_int8_mixed_matmul_workspace(M, K)
- *   exceeds SQ_MIXED_SCRATCH_BYTES (e.g. M x K above ~33.5 M elements),
+ *   Returns SQ_ERR_WORKSPACE when sq_int8_mixed_matmul_workspace(M, N, K)
+ *   exceeds SQ_MIXED_SCRATCH_BYTES (M = 2048, N = K = 4096 needs about
+ *   11.6 MB; with N = K = 4096 up to about 6500 rows fit),
  *   SQ_ERR_HIP when the array's device address cannot be obtained (looked up
  *   once per GPU, with that GPU current, on the first call there).
  * Every call on a GPU uses that GPU's one array: calls that overlap on one

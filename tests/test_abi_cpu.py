@@ -118,9 +118,16 @@ def test_gemm_validation():
 
 def test_mixed_validation():
     L = sq.lib()
-    need = L.sq_int8_mixed_matmul_workspace(2048, 4096)
+    need = L.sq_int8_mixed_matmul_workspace(2048, 4096, 4096)
     assert need >= 2048 * 4096 + 2048 * 4 + 3 * 4096 * 4
     assert need % 256 == 0
+    # the documented layout: parts back to back, 256-byte rounded, the side
+    # operands sized for min(K, SQ_MIXED_SIDE_COLS) columns
+    for M, N, K in ((2048, 4096, 4096), (1, 1, 16), (300, 520, 1040), (7, 3, 64)):
+        assert L.sq_int8_mixed_matmul_workspace(M, N, K) == \
+            sq.int8_mixed_workspace_parts(M, N, K)["total"]
+    assert sq.int8_mixed_workspace_parts(7, 3, 64)["side_cols"] == 64
+    assert sq.int8_mixed_workspace_parts(7, 3, 4096)["side_cols"] == 128
 
     def call(thr=6.0, ws=FAKE, wsb=need, K=4096, x=FAKE):
         return L.sq_int8_mixed_matmul(x, 2048, K, FAKE, FAKE, FAKE, 4096, thr, ws, wsb, FAKE,
@@ -157,14 +164,14 @@ def test_mixed_noalloc_validation():
     assert call(ydt=7) == DTYPE
     assert call(M=0, x=None, y=None) == OK
     assert call(M=8192, K=8192) == WORKSPACE              # 64 MiB of int8 rows alone
-    # the largest M for K = 4096 that fits, and one row more
+    # the largest M for N = K = 4096 that fits, and one row more
     M = 1
-    while L.sq_int8_mixed_matmul_workspace(M + 1, 4096) <= cap:
+    while L.sq_int8_mixed_matmul_workspace(M + 1, 4096, 4096) <= cap:
         M += 1
-    assert L.sq_int8_mixed_matmul_workspace(M, 4096) <= cap < \
-        L.sq_int8_mixed_matmul_workspace(M + 1, 4096)
+    assert L.sq_int8_mixed_matmul_workspace(M, 4096, 4096) <= cap < \
+        L.sq_int8_mixed_matmul_workspace(M + 1, 4096, 4096)
     assert call(M=M + 1, K=4096) == WORKSPACE
-    assert M >= 8000   # the 2048 x 4096 LLM.int8() workload fits with room
+    assert M >= 6000   # the 2048 x 4096 LLM.int8() workload fits with room
 
 
 def test_zero_length_rows_are_rejected_before_any_pointer_is_used():

@@ -148,7 +148,8 @@ def test_llm_int8_2048(torch):
     log("llm_int8_2048")
     wq, ws, wq_o, ws_o = _weights(torch, W, None)
     M, K = X.shape
-    work = torch.full((sq.int8_mixed_matmul_workspace(M, K),), 0xA5, dtype=torch.uint8,
+    N = W.shape[0]
+    work = torch.full((sq.int8_mixed_matmul_workspace(M, N, K),), 0xA5, dtype=torch.uint8,
                       device="cuda")
     y, acc, cnt = sq.int8_mixed_matmul(dev(X, torch), wq, ws, dev(W, torch), 6.0,
                                        workspace=work, with_count=True, with_acc=True)
@@ -157,9 +158,11 @@ def test_llm_int8_2048(torch):
     assert int(host(cnt, torch)[0]) == 6
     # the intermediates of the decomposition ([INT8-expl] §2.2), from the
     # workspace's documented layout: O, X~q, the row steps, the column
-    # maxima and mask, and the int32 sums of the int8 part
+    # maxima and mask, the side operands (x and w in the outlier columns,
+    # fp32), and the int32 sums of the int8 part
     wb = host(work, torch)
-    off = sq.int8_mixed_workspace_parts(M, K)
+    off = sq.int8_mixed_workspace_parts(M, N, K)
+    assert work.numel() == off["total"]
     n_o = int(wb[off["count"]:off["count"] + 4].view(np.int32)[0])
     assert n_o == 6
     assert_bits_equal(wb[off["idx"]:off["idx"] + 4 * n_o].view(np.int32), r["idx"], "O list")
@@ -172,6 +175,10 @@ def test_llm_int8_2048(torch):
     mask = np.ones(K, np.float32)
     mask[r["idx"]] = 0.0
     assert_bits_equal(wb[off["mask"]:off["mask"] + 4 * K].view(np.float32), mask, "column mask")
+    xs_side = wb[off["x_side"]:off["x_side"] + 4 * n_o * M].view(np.float32).reshape(n_o, M)
+    ws_side = wb[off["w_side"]:off["w_side"] + 4 * n_o * N].view(np.float32).reshape(n_o, N)
+    assert_bits_equal(xs_side, X[:, r["idx"]].T.astype(np.float32), "side activations")
+    assert_bits_equal(ws_side, W[:, r["idx"]].T.astype(np.float32), "side weights")
     assert_bits_equal(host(acc, torch), r["acc"], "acc")
     assert_bits_equal(host(y, torch), r["y"], "y")
     print(f"\nllm_int8_2048 rel. error vs fp64: {_rel_err(r['y'], X, W):.5f}")

@@ -156,7 +156,7 @@ def test_llm_int8(torch):
     log(f"determinism llm.int8 M{M} N{N} K{K}")
 
     def run(fill):
-        wsp = _filled(torch, (sq.int8_mixed_matmul_workspace(M, K),), torch.uint8, fill)
+        wsp = _filled(torch, (sq.int8_mixed_matmul_workspace(M, N, K),), torch.uint8, fill)
         y, cnt = sq.int8_mixed_matmul(X, wq, ws, W16, 6.0, workspace=wsp, with_count=True)
         y32 = sq.int8_mixed_matmul(X, wq, ws, W16, 6.0, out_dtype=torch.float32)
         return [y, cnt, y32]

@@ -91,7 +91,7 @@ def test_graph_llm_int8(torch):
     cfg = synth.llm_int8_2048(M=256, N=512, K=1024)
     X, W = dev(cfg["X"], torch), dev(cfg["W"], torch)
     wq, ws = sq.smooth_weights(W)
-    ws_buf = torch.empty(sq.int8_mixed_matmul_workspace(256, 1024), dtype=torch.uint8,
+    ws_buf = torch.empty(sq.int8_mixed_matmul_workspace(256, 512, 1024), dtype=torch.uint8,
                          device="cuda")
 
     def run():

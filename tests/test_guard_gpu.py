@@ -181,7 +181,7 @@ def test_mixed_guards(torch, M, N, K, n_dims, tile):
     cfg = synth.llm_int8_2048(M=M, N=N, K=K, seed=M + N, n_dims=n_dims)
     X, W = dev(cfg["X"], torch), dev(cfg["W"], torch)
     wq, ws = sq.smooth_weights(W)
-    need = L.sq_int8_mixed_matmul_workspace(M, K)
+    need = L.sq_int8_mixed_matmul_workspace(M, N, K)
     gw = Guarded(torch, need)
     gy, ga, gc = Guarded(torch, M * N * 2), Guarded(torch, M * N * 4), Guarded(torch, 4)
     log(f"guards mixed M={M} N={N} K={K} dims={n_dims} tile={tile}")

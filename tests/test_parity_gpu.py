@@ -198,7 +198,9 @@ def test_gemm_extremal_values(torch):
 # The side-term GEMM: 256 x 128 tiles (ragged M and N), 128 x 128 tiles when
 # forced, the non-pipelined tile when K % 128 != 0, more than 32 outlier
 # columns (threshold 0.5: the side operands are staged 32 columns at a time)
-# on each of the three kernels.
+# on each of the three kernels.  Up to SQ_MIXED_SIDE_COLS (128) outlier
+# columns the side operands come from the compact copies, above it (every
+# column at threshold 0.5 with K >= 256; 129 planted) straight from x and w.
 @pytest.mark.parametrize("M,N,K,thr,tile,n_dims", [
     (300, 200, 512, 6.0, None, 6), (64, 130, 256, float("inf"), None, 6),
     (40, 96, 128, 0.5, None, 6), (2048, 256, 4096, 6.0, None, 6), (300, 200, 512, 6.0, "2", 6),
@@ -206,7 +208,10 @@ def test_gemm_extremal_values(torch):
     (130, 200, 256, 0.5, "2", 6),
     # |O| at the 32-column chunk boundary and one past it (planted dimensions)
     (300, 200, 512, 6.0, None, 32), (300, 200, 512, 6.0, None, 33),
-    (100, 150, 208, 6.0, None, 33)])
+    (100, 150, 208, 6.0, None, 33),
+    # the compact side operands' capacity and one past it
+    (300, 200, 512, 6.0, None, 128), (300, 200, 512, 6.0, None, 129),
+    (260, 136, 384, 6.0, "2", 129)])
 def test_mixed_parity(torch, M, N, K, thr, tile, n_dims):
     import synth
 

@@ -38,7 +38,7 @@ def test_noalloc_matches_workspace_form(torch):
         cfg = synth.llm_int8_2048(M=M, N=N, K=K, seed=seed, n_dims=n_dims)
         X, W = dev(cfg["X"], torch), dev(cfg["W"], torch)
         wq, ws = sq.smooth_weights(W)
-        need = L.sq_int8_mixed_matmul_workspace(M, K)
+        need = L.sq_int8_mixed_matmul_workspace(M, N, K)
         work = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
         outs = []
         for form in ("workspace", "noalloc"):

@@ -48,7 +48,7 @@ SIGNATURES = {
     "sq_smooth_weights_folded": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P]),
     "sq_quantize_act": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "sq_gemm_i8_dequant": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _I, _P, _P]),
-    "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64]),
+    "sq_int8_mixed_matmul_workspace": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "sq_int8_mixed_matmul": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, ctypes.c_size_t,
                                   _P, _I, _P, _P, _P]),
     "sq_int8_mixed_matmul_noalloc": (_I, [_P, _I64, _I64, _P, _P, _P, _I64, _F, _P, _I, _P, _P,
@@ -245,21 +245,29 @@ def gemm_i8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, with_acc=False, ou
     return (y, acc) if with_acc else y
 
 
-def int8_mixed_matmul_workspace(M, K) -> int:
-    return int(lib().sq_int8_mixed_matmul_workspace(M, K))
+SQ_MIXED_SIDE_COLS = 128
 
 
-def int8_mixed_workspace_parts(M, K):
+def int8_mixed_matmul_workspace(M, N, K) -> int:
+    return int(lib().sq_int8_mixed_matmul_workspace(M, N, K))
+
+
+def int8_mixed_workspace_parts(M, N, K):
     """Byte offsets of the parts the workspace holds on return (include/sq.h):
     xq [M,K] int8, x_scale [M], colmax [K], mask [K] fp32, idx [K] int32,
-    count int32."""
+    count int32, then (written when |O| <= side_cols) the side operands
+    x_side [side_cols, M] and w_side [side_cols, N] fp32."""
     r = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    off = {"xq": 0}
+    cap = min(K, SQ_MIXED_SIDE_COLS)
+    off = {"xq": 0, "side_cols": cap}
     off["x_scale"] = off["xq"] + r(M * K)
     off["colmax"] = off["x_scale"] + r(4 * M)
     off["mask"] = off["colmax"] + r(4 * K)
     off["idx"] = off["mask"] + r(4 * K)
     off["count"] = off["idx"] + r(4 * K)
+    off["x_side"] = off["count"] + 256
+    off["w_side"] = off["x_side"] + r(4 * cap * M)
+    off["total"] = off["w_side"] + r(4 * cap * N)
     return off
 
 
@@ -274,7 +282,7 @@ def int8_mixed_matmul(x, wq, w_scale, w_f16, threshold=6.0, out_dtype=None, work
     _check(w_f16, "w_f16", (torch.float16,), 2)
     M, K = x.shape
     N = wq.shape[0]
-    need = int8_mixed_matmul_workspace(M, K)
+    need = int8_mixed_matmul_workspace(M, N, K)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     y = torch.empty((M, N), dtype=out_dtype or torch.float16, device=x.device)

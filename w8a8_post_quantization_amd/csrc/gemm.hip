@@ -46,6 +46,15 @@ __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// One step of the LLM.int8() side sum, acc + x w with x and w fp16 values
+// (widened exactly): their product has at most 22 significant bits and lies
+// between 2^-48 and 2^32 in magnitude (or is 0), so it is exact in fp32 and
+// the fused multiply-add's one rounding is the rounding of the addition:
+// the same value as fl(acc + fl(x w)), in one instruction instead of two.
+__device__ __forceinline__ float side_fma(float x, float w, float acc) {
+    return __builtin_fmaf(x, w, acc);
+}
+
 struct GemmArgs {
     const int8_t *xq;
     const int8_t *wq;
@@ -59,6 +68,9 @@ struct GemmArgs {
     const uint16_t *w16;
     const int32_t *idx;
     const int32_t *count;
+    const float *xo;       // compact side operands, used when |O| <= side_cap
+    const float *wo;
+    int side_cap;
     int tiles_n;
     int tiles_m;
     int xcd_gm, xcd_gn;  // XCD grid of the tile mapping (tile_of), or 0: row-major
@@ -92,17 +104,22 @@ struct SideLds {
     static constexpr int BYTES = 32 * (XS + WS) * 4;
 };
 
-// Stage outlier columns t0 .. t0 + tn - 1 (tn <= 32) of the tile's 16-bit
+// Stage outlier columns t0 .. t0 + tn - 1 (tn <= 32) of the tile's
 // activation rows and weight rows into LDS as floats (SideLds layout; only
 // columns t < tn are written).  Thread tid serves activation row tid % BM
 // for columns tid / BM, tid / BM + NT / BM, ... and weight row tid % BN for
-// columns tid / BN, tid / BN + NT / BN, ...: the column of each gather is the
-// same across a wave (BM, BN multiples of 64), so its index is one scalar
-// load, dead columns cost no gather, and the loads of a group of four
-// columns are all issued before the first is written.
+// columns tid / BN, tid / BN + NT / BN, ...: the column is the same across a
+// wave (BM, BN multiples of 64), dead columns cost no load, and the loads of
+// a group of four columns are all issued before the first is written.  With
+// `compact` the values come from the gathered side operands (p.xo, p.wo:
+// one column's rows are contiguous, so a wave's load is coalesced); else
+// each is a 2-byte gather from the fp16 rows at the column's index (a
+// scalar load).  With `pre`, px and pw hold the compact values of the first
+// group of the first chunk, fetched by side_prefetch at kernel start.
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *wo, int m0,
-                                           int n0, int t0, int tn) {
+                                           int n0, int t0, int tn, bool compact, bool pre,
+                                           const float (&px)[4], const float (&pw)[4]) {
     static_assert(BM % 64 == 0 && BN % 64 == 0 && NT % BM == 0 && NT % BN == 0,
                   "side staging");
     constexpr int PX = NT / BM, PW = NT / BN, G = 4;
@@ -111,20 +128,43 @@ __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *
     const int rx = tid % BM, rw = tid % BN;
     const int cx = __builtin_amdgcn_readfirstlane(tid / BM);
     const int cw = __builtin_amdgcn_readfirstlane(tid / BN);
-    const uint16_t *xr = p.x16 + (int64_t)(m0 + rx < p.M ? m0 + rx : p.M - 1) * p.K;
-    const uint16_t *wr = p.w16 + (int64_t)(n0 + rw < p.N ? n0 + rw : p.N - 1) * p.K;
+    const int mr = m0 + rx < p.M ? m0 + rx : p.M - 1;
+    const int nr = n0 + rw < p.N ? n0 + rw : p.N - 1;
+    const uint16_t *xr = p.x16 + (int64_t)mr * p.K;
+    const uint16_t *wr = p.w16 + (int64_t)nr * p.K;
+    const float *xc = p.xo + (int64_t)t0 * p.M + mr;
+    const float *wc = p.wo + (int64_t)t0 * p.N + nr;
     const int32_t *idx = p.idx + t0;
     for (int q = 0; q * G * PX < tn || q * G * PW < tn; ++q) {
         float vx[G], vw[G];
+        if (compact && pre && t0 == 0 && q == 0) {
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int t = cx + PX * (q * G + k);
-            vx[k] = t < tn ? h2f(xr[idx[t]]) : 0.0f;
-        }
+            for (int k = 0; k < G; ++k) {
+                vx[k] = px[k];
+                vw[k] = pw[k];
+            }
+        } else if (compact) {
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int t = cw + PW * (q * G + k);
-            vw[k] = t < tn ? h2f(wr[idx[t]]) : 0.0f;
+            for (int k = 0; k < G; ++k) {
+                const int t = cx + PX * (q * G + k);
+                vx[k] = t < tn ? xc[(int64_t)t * p.M] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const int t = cw + PW * (q * G + k);
+                vw[k] = t < tn ? wc[(int64_t)t * p.N] : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const int t = cx + PX * (q * G + k);
+                vx[k] = t < tn ? h2f(xr[idx[t]]) : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const int t = cw + PW * (q * G + k);
+                vw[k] = t < tn ? h2f(wr[idx[t]]) : 0.0f;
+            }
         }
 #pragma unroll
         for (int k = 0; k < G; ++k) {
@@ -137,6 +177,29 @@ __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *
             if (t < tn) wo[t * WS + rw] = vw[k];
         }
     }
+}
+
+// The first group of stage_side's compact side values (columns
+// tid / BM + k NT / BM and tid / BN + k NT / BN, k < 4) read at kernel start,
+// before |O| is known: the compact arrays hold side_cap columns, so every
+// read is in bounds, and staging keeps only the columns below |O|.  Valid
+// (returns true) when p.xo is set and side_cap covers the group.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ bool side_prefetch(const GemmArgs &p, int m0, int n0, float (&px)[4],
+                                              float (&pw)[4]) {
+    constexpr int PX = NT / BM, PW = NT / BN, G = 4;
+    constexpr int SPAN = (PX > PW ? PX : PW) * G;
+    if (!p.xo || p.side_cap < SPAN) return false;
+    const int tid = threadIdx.x;
+    const int mr = m0 + tid % BM < p.M ? m0 + tid % BM : p.M - 1;
+    const int nr = n0 + tid % BN < p.N ? n0 + tid % BN : p.N - 1;
+    const int cx = tid / BM, cw = tid / BN;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+        px[k] = p.xo[(int64_t)(cx + PX * k) * p.M + mr];
+        pw[k] = p.wo[(int64_t)(cw + PW * k) * p.N + nr];
+    }
+    return true;
 }
 
 // Each thread fetches (at most) one row step and one column step at kernel
@@ -206,10 +269,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
         float *xo = reinterpret_cast<float *>(smem);
         float *wo = xo + 32 * L::XS;
         const int cnt = *p.count;
+        const bool compact = cnt <= p.side_cap;
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn);
+            const float none[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn, compact, false, none, none);
             __syncthreads();
             // column by column, so each output still sums in ascending order
             for (int t = 0; t < tn; ++t) {
@@ -227,8 +292,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
                         for (int j = 0; j < FN; ++j)
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
-                                const float prod = xq[q] * wv[j];
-                                side[i][j][4 * g + q] = side[i][j][4 * g + q] + prod;
+                                side[i][j][4 * g + q] = side_fma(xq[q], wv[j], side[i][j][4 * g + q]);
                             }
                     }
             }
@@ -502,7 +566,8 @@ template <int BM, int BN, int WM, int WN, int YDT, bool SIDE, typename AccV>
 __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                                             AccV (&acc)[BN / WN / 32][BM / WM / 32],
                                             int8_t *smem, const float *sx, const float *sw,
-                                            int m0, int n0) {
+                                            int m0, int n0, bool pre,
+                                            const float (&px)[4], const float (&pw)[4]) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int NT = 64 * WM * WN;
@@ -523,10 +588,11 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
         float *xo = reinterpret_cast<float *>(smem);
         float *wo = xo + 32 * L::XS;
         const int cnt = *p.count;
+        const bool compact = cnt <= p.side_cap;
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn);
+            stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn, compact, pre, px, pw);
             __syncthreads();
             // column by column, so each output still sums in ascending order
             for (int t = 0; t < tn; ++t) {
@@ -544,8 +610,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                         for (int j = 0; j < FM; ++j)
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
-                                const float prod = xv[j] * wq[q];
-                                side[i][j][4 * g + q] = side[i][j][4 * g + q] + prod;
+                                side[i][j][4 * g + q] = side_fma(xv[j], wq[q], side[i][j][4 * g + q]);
                             }
                     }
             }
@@ -732,6 +797,11 @@ gemm_pp(GemmArgs p) {
     const int M = p.M, N = p.N, K = p.K;
     TileScales<BM, BN> scl;
     scl.load(p, m0, n0);
+    // LLM.int8(): the side term's first operand group, fetched now so its
+    // latency hides under the main loop instead of following it.
+    float spx[4] = {0.0f, 0.0f, 0.0f, 0.0f}, spw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool spre = false;
+    if constexpr (SIDE) spre = side_prefetch<BM, BN, 64 * NW>(p, m0, n0, spx, spw);
 
     const int8_t *a_src[LA];
     const int8_t *b_src[LB];
@@ -849,7 +919,7 @@ gemm_pp(GemmArgs p) {
         wait_vmcnt<0>();
         scl.publish(sx, sw);
         __syncthreads();
-        epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0);
+        epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, spre, spx, spw);
         return;
     } else {
     // Main loop.  Its two halves are branch-free so the scheduler can
@@ -899,7 +969,7 @@ gemm_pp(GemmArgs p) {
     wait_vmcnt<0>();
     scl.publish(sx, sw);
     __syncthreads();  // steps visible; the side term may reuse the ring
-    epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0);
+    epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, spre, spx, spw);
     }
 }
 
@@ -1237,6 +1307,7 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         // With the side term 256 x 256 tiles would need the side sums next
         // to 128 accumulator registers: the 256-row choices take 256 x 128.
         a.x16 = side->x16; a.w16 = side->w16; a.idx = side->idx; a.count = side->count;
+        a.xo = side->xo; a.wo = side->wo; a.side_cap = side->xo && side->wo ? side->cap : -1;
         if (pipe && tile < 2) launch_pipe_t<256, 128, 4, 2, 3, 3, true>(a, y_dt, stream);
         else if (pipe) launch_pipe_t<128, 128, 2, 2, 2, 2, true>(a, y_dt, stream);
         else launch_tile_t<128, 128, 2, 2, true>(a, y_dt, stream);

@@ -49,9 +49,129 @@ __device__ __forceinline__ void load_mul(const float *__restrict__ mul, int64_t 
 
 extern __shared__ float4 smul4[];
 
+// LLM.int8() mask mode (ol.on): the column multiplier is 1 for a kept
+// column and 0 for an outlier column, derived where it is read from the
+// column abs-max (mul then points to it): a column is an outlier dimension
+// when its largest |x| reaches the threshold (the xdnf.cn LLM.int8()
+// explainer, §2.2 and §4.1).
+__device__ __forceinline__ float keep(float colmax, float thr) {
+    return colmax >= thr ? 0.0f : 1.0f;
+}
+__device__ __forceinline__ float4 keep4(float4 c, float thr) {
+    return make_float4(keep(c.x, thr), keep(c.y, thr), keep(c.z, thr), keep(c.w, thr));
+}
+
+// The extra blocks of a masked quantizer (the last ol.blocks blocks of the
+// grid, after the row blocks: the row blocks keep the even spread over the
+// compute units they have without them, measured 3 us faster for the
+// 2048 x 4096 activations than with the extra blocks first).  Each
+// rebuilds the ascending outlier list from the column maxima: a pass covers
+// 256 * C columns, thread t the C consecutive columns from t * C, loaded as
+// four 16-byte vectors with no condition (K % 16 == 0, so a thread's columns
+// are all in range or all past the end, and those past it re-read the last
+// 16; a load under a lane-dependent condition would make the compiler wait
+// for each one before the next); a wave prefix sum of the per-thread hit counts plus the earlier
+// waves' totals gives each thread its first list slot.  Block 0 writes the
+// mask, the list and |O|; every block keeps the first cap entries in LDS and,
+// when |O| <= cap, gathers its share of the side operands (element e of the
+// cnt (M + N) values, e = b * 256 + tid, b * 256 + tid + 256 * blocks, ...;
+// consecutive threads take consecutive rows of one column, so the stores are
+// coalesced).  Called by every thread of the block.
+__device__ void outlier_side_block(const float *__restrict__ colmax,
+                                   const uint16_t *__restrict__ x16, int64_t K,
+                                   const OutlierList &ol, int b) {
+    const int64_t M = ol.M;
+    constexpr int C = 16;
+    __shared__ int wave_tot[4];
+    __shared__ int s_idx[kSideColsMax];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool lead = b == 0;
+    int base = 0;  // list entries of earlier passes (the same in every thread)
+    for (int64_t j0 = 0; j0 < K; j0 += 256 * C) {
+        const int64_t jb = j0 + (int64_t)tid * C;
+        const float4 *src = reinterpret_cast<const float4 *>(colmax + (jb < K ? jb : K - C));
+        float v[C];
+#pragma unroll
+        for (int i = 0; i < C / 4; ++i) {
+            const float4 f = src[i];
+            v[4 * i] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+        uint32_t hits = 0;
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+            if (jb + i < K && v[i] >= ol.thr) hits |= 1u << i;
+        const int n = __popc(hits);
+        int incl = n;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        if (lane == 63) wave_tot[wave] = incl;
+        __syncthreads();
+        int slot = base + incl - n;
+        for (int w = 0; w < wave; ++w) slot += wave_tot[w];
+        base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (jb + i >= K) break;
+            const bool hit = (hits >> i) & 1u;
+            if (lead) {
+                ol.mask[jb + i] = hit ? 0.0f : 1.0f;
+                if (hit) ol.idx[slot] = (int32_t)(jb + i);
+            }
+            if (hit && slot < ol.cap) s_idx[slot] = (int32_t)(jb + i);
+            slot += hit;
+        }
+        __syncthreads();  // wave_tot is rewritten by the next pass; s_idx complete
+    }
+    if (lead && tid == 0) {
+        *ol.count = base;
+        if (ol.count_out) *ol.count_out = base;
+    }
+    const int64_t cnt = base;
+    if (cnt == 0 || cnt > ol.cap) return;  // nothing, or the GEMM reads x and w directly
+    // Four elements per thread per round, their loads issued together
+    // (indices past the end clamped to the last element, whose value is
+    // then not stored).
+    const int64_t nx = cnt * M, total = nx + cnt * ol.N;
+    const int64_t stride = (int64_t)ol.blocks * 256;
+    constexpr int U = 4;
+    for (int64_t e0 = (int64_t)b * 256 + tid; e0 < total; e0 += U * stride) {
+        float val[U];
+        int64_t at[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t e = e0 + u * stride;
+            e = e < total ? e : total - 1;
+            const bool isx = e < nx;
+            const int64_t f = isx ? e : e - nx, rows = isx ? M : ol.N;
+            const int64_t t = f / rows, r = f - t * rows;
+            const uint16_t *src = isx ? x16 : ol.w16;
+            val[u] = (float)__builtin_bit_cast(_Float16, src[r * K + s_idx[t]]);
+            at[u] = e;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (e0 + u * stride >= total) break;
+            const int64_t e = at[u];
+            if (e < nx) ol.xo[e] = val[u];
+            else ol.wo[e - nx] = val[u];
+        }
+    }
+}
+
+// One 16-byte vector of a row widened to fp32, times the row multiplier rm
+// (HAS_ROW) and the column multipliers (HAS_MUL: from LDS when staged, else
+// from global memory; in the LLM.int8() mask mode those are the column
+// maxima, turned into 1 / 0 here).
 template <int DT, bool HAS_MUL, bool MUL_LDS, bool HAS_ROW = false>
 __device__ __forceinline__ void scaled(const uint4 &raw, const float *__restrict__ mul,
-                                       int64_t e0, float *v, float rm = 1.0f) {
+                                       int64_t e0, float *v, float rm = 1.0f,
+                                       const OutlierList *ol = nullptr) {
     constexpr int V = Vec<DT>::n;
     widen16<DT>(raw, v);
     if constexpr (HAS_ROW) {
@@ -71,6 +191,10 @@ __device__ __forceinline__ void scaled(const uint4 &raw, const float *__restrict
             }
         } else {
             load_mul<DT>(mul, e0, m);
+            if (ol && ol->on) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) m[i] = keep(m[i], ol->thr);
+            }
         }
 #pragma unroll
         for (int i = 0; i < V; ++i) v[i] = v[i] * m[i];
@@ -168,16 +292,29 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                                                          const float *__restrict__ static_scale,
                                                          int8_t *__restrict__ q,
                                                          float *__restrict__ scale,
-                                                         int rows_per_wave) {
+                                                         int rows_per_wave, OutlierList ol) {
     constexpr int V = Vec<DT>::n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (!DYN && blockIdx.x == 0 && threadIdx.x == 0) scale[0] = static_scale[0];
+    if (ol.on) {
+        const int first = (int)gridDim.x - ol.blocks;
+        if ((int)blockIdx.x >= first) {
+            outlier_side_block(mul_g, reinterpret_cast<const uint16_t *>(x), K, ol,
+                               (int)blockIdx.x - first);
+            return;
+        }
+    }
+    const int64_t bid = blockIdx.x;  // row block
+    if (!DYN && bid == 0 && threadIdx.x == 0) scale[0] = static_scale[0];
     // The multiplier's address space is fixed at compile time (an LDS or a
     // global pointer), so its reads are ds_read / global_load, never flat.
     const float *mul = mul_g;
     if constexpr (HAS_MUL && MUL_LDS) {
         const float4 *src = reinterpret_cast<const float4 *>(mul_g);
-        for (int64_t i = threadIdx.x; i < K / 4; i += 256) smul4[i] = src[i];
+        if (ol.on) {
+            for (int64_t i = threadIdx.x; i < K / 4; i += 256) smul4[i] = keep4(src[i], ol.thr);
+        } else {
+            for (int64_t i = threadIdx.x; i < K / 4; i += 256) smul4[i] = src[i];
+        }
         __syncthreads();
     }
     const int64_t nvec = K / V;
@@ -186,7 +323,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
     // Rows of this wave: ((block * rows_per_wave + i) * 4 + wave).  The wave
     // index is made explicitly uniform so row bounds become scalar branches.
     const int64_t wv = __builtin_amdgcn_readfirstlane(wave);
-    auto row_of = [&](int i) { return ((int64_t)blockIdx.x * rows_per_wave + i) * 4 + wv; };
+    auto row_of = [&](int i) { return (bid * rows_per_wave + i) * 4 + wv; };
 
     if constexpr (DYN && ITS > 0) {
         // Two rows in flight per wave: row i + 1's loads are issued before
@@ -208,7 +345,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 const int64_t vi = lane + (int64_t)it * kWave;
                 const int64_t vc = vi < nvec ? vi : nvec - 1;
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(b[it], mul, vc * V, v, rm);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(b[it], mul, vc * V, v, rm, &ol);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
@@ -227,7 +364,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
                 const int64_t vi = lane + (int64_t)it * kWave;
                 if (vi < nvec) {
                     float v[V];
-                    scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm);
+                    scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(raw, mul, vi * V, v, rm, &ol);
                     store_q<DT, FP8, false, NTS>(qr, vi * V, v, inv);
                 }
             }
@@ -262,7 +399,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             float a = 0.0f;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm, &ol);
 #pragma unroll
                 for (int i = 0; i < V; ++i) a = fmaxf(a, fabsf(v[i]));
             }
@@ -272,7 +409,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
             if (lane == 0) scale[r] = a / QMax<FP8>::v;
             for (int64_t vi = lane; vi < nvec; vi += kWave) {
                 float v[V];
-                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm);
+                scaled<DT, HAS_MUL, MUL_LDS, HAS_ROW>(xr[vi], mul, vi * V, v, rm, &ol);
                 store_q<DT, FP8, false, NTS>(qr, vi * V, v, inv);
             }
         } else {
@@ -297,10 +434,19 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
                                                               const float *__restrict__ row_mul,
                                                               const float *__restrict__ static_scale,
                                                               int8_t *__restrict__ q,
-                                                              float *__restrict__ scale) {
+                                                              float *__restrict__ scale,
+                                                              OutlierList ol) {
     constexpr int V = Vec<DT>::n;
     __shared__ float wmax[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (ol.on) {
+        const int first = (int)gridDim.x - ol.blocks;
+        if ((int)blockIdx.x >= first) {
+            outlier_side_block(mul, reinterpret_cast<const uint16_t *>(x), K, ol,
+                               (int)blockIdx.x - first);
+            return;
+        }
+    }
     const int64_t r = blockIdx.x;
     if (!DYN && r == 0 && tid == 0) scale[0] = static_scale[0];
     const int64_t nvec = K / V;
@@ -313,6 +459,14 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
         const int64_t vc = vi < nvec ? vi : nvec - 1;
         raw[it] = ld_nt(xr + vc);
         if constexpr (HAS_MUL) load_mul<DT>(mul, vc * V, m[it]);
+    }
+    if constexpr (HAS_MUL) {
+        if (ol.on) {
+#pragma unroll
+            for (int it = 0; it < ITS; ++it)
+#pragma unroll
+                for (int i = 0; i < V; ++i) m[it][i] = keep(m[it][i], ol.thr);
+        }
     }
     const float rm = HAS_ROW ? row_mul[r] : 1.0f;
     float inv;
@@ -363,17 +517,27 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
 template <int DT, bool HAS_MUL, bool DYN, bool HAS_ROW = false, bool FP8 = false>
 static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
                      const float *static_scale, int8_t *q, float *scale, hipStream_t stream,
-                     const float *row_mul = nullptr) {
+                     const float *row_mul = nullptr, const OutlierList *olp = nullptr) {
+    OutlierList ol = olp ? *olp : OutlierList{};
+    // LLM.int8(): extra blocks for the outlier list and the side operands,
+    // about one per 128 rows of x and w (a few gathered values per thread
+    // for a few outlier columns).
+    int64_t extra = 0;
+    if (ol.on) {
+        extra = (ol.M + ol.N) / 128;
+        extra = extra < 1 ? 1 : extra > 64 ? 64 : extra;
+        ol.blocks = (int)extra;
+    }
     auto *xv = reinterpret_cast<const uint4 *>(x);
     const int64_t nvec = K / Vec<DT>::n;
     // Fewer rows than ~2 waves per SIMD of the chip, and long enough rows:
     // a block per row.
     if (rows < 2048 && nvec >= 256 && nvec <= 8 * 256) {
         const int64_t its = (nvec + 255) / 256;
-        dim3 grid((unsigned)rows), block(256);
+        dim3 grid((unsigned)(rows + extra)), block(256);
 #define SQ_B(ITS) \
     quant_row_block_kernel<DT, HAS_MUL, DYN, ITS, HAS_ROW, FP8><<<grid, block, 0, stream>>>(   \
-        xv, K, mul, row_mul, static_scale, q, scale)
+        xv, K, mul, row_mul, static_scale, q, scale, ol)
         if (its <= 1) SQ_B(1);
         else if (its <= 2) SQ_B(2);
         else if (its <= 4) SQ_B(4);
@@ -395,12 +559,12 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     const int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
     const bool mul_lds = HAS_MUL && K <= kMulLds;
     const size_t shmem = mul_lds ? (size_t)K * sizeof(float) : 0;
-    dim3 grid((unsigned)blocks), block(256);
+    dim3 grid((unsigned)(blocks + extra)), block(256);
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
 #define SQ_Q(ITS, LDS, NT)                                                                      \
     quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8, NT><<<grid, block, shmem, stream>>>( \
-        xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw)
+        xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw, ol)
 #define SQ_QL(ITS)                                    \
     do {                                              \
         if (mul_lds && nts) SQ_Q(ITS, true, true);    \
@@ -435,7 +599,11 @@ static void launch_dt_fp8(const void *x, int64_t rows, int64_t K, const float *m
 template <int DT>
 static void launch_dt(const void *x, int64_t rows, int64_t K, const float *mul, int dynamic,
                       const float *static_scale, int8_t *q, float *scale, hipStream_t stream,
-                      const float *row_mul) {
+                      const float *row_mul, const OutlierList *ol) {
+    if (ol) {  // LLM.int8(): per-row steps over the kept columns
+        launch_q<DT, true, true>(x, rows, K, mul, static_scale, q, scale, stream, nullptr, ol);
+        return;
+    }
     if (row_mul) {  // weights only: per-row steps
         if (mul) launch_q<DT, true, true, true>(x, rows, K, mul, static_scale, q, scale, stream, row_mul);
         else launch_q<DT, false, true, true>(x, rows, K, mul, static_scale, q, scale, stream, row_mul);
@@ -466,16 +634,16 @@ void launch_quant_rows_fp8(const void *x, int dt, int64_t rows, int64_t K, const
 
 void launch_quant_rows(const void *x, int dt, int64_t rows, int64_t K, const float *mul,
                        int dynamic, const float *static_scale, int8_t *q, float *scale,
-                       hipStream_t stream, const float *row_mul) {
+                       hipStream_t stream, const float *row_mul, const OutlierList *ol) {
     if (rows == 0) {
         if (!dynamic)  // the per-tensor step is still reported
             launch_copy_f32(static_scale, scale, stream);
         return;
     }
     if (K <= 0) return;  // rejected by the C ABI: the kernels clamp to the last vector
-    if (dt == F32) launch_dt<F32>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
-    else if (dt == F16) launch_dt<F16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
-    else launch_dt<BF16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul);
+    if (dt == F32) launch_dt<F32>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul, ol);
+    else if (dt == F16) launch_dt<F16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul, ol);
+    else launch_dt<BF16>(x, rows, K, mul, dynamic, static_scale, q, scale, stream, row_mul, ol);
 }
 
 }  // namespace sq

@@ -209,60 +209,10 @@ void launch_static_scale(const float *act_amax, const float *inv_s, int64_t K, f
     static_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(act_amax, inv_s, K, qmax, out);
 }
 
-// LLM.int8() outlier list: O = ascending { j : colmax_j >= threshold }
-// (colmax is the column abs-max, so this is "some |x| reaches the
-// threshold"), mask_j = 0 for j in O else 1, plus |O|.  One block scans K in
-// chunks of 1024 with a ballot prefix count.
-__global__ __launch_bounds__(1024) void outlier_list_kernel(const float *__restrict__ colmax,
-                                                            int64_t K, float threshold,
-                                                            float *__restrict__ mask,
-                                                            int32_t *__restrict__ idx,
-                                                            int32_t *__restrict__ count,
-                                                            int32_t *__restrict__ count_out) {
-    __shared__ int wave_cnt[16];
-    __shared__ int base_s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) base_s = 0;
-    __syncthreads();
-    for (int64_t j0 = 0; j0 < K; j0 += 1024) {
-        const int64_t j = j0 + threadIdx.x;
-        const bool hit = j < K && colmax[j] >= threshold;
-        const uint64_t bal = __ballot(hit);
-        const int below = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_cnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = base_s;
-        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-        if (j < K) {
-            mask[j] = hit ? 0.0f : 1.0f;
-            if (hit) idx[off + below] = (int32_t)j;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int t = 0;
-            for (int w = 0; w < 16; ++w) t += wave_cnt[w];
-            base_s += t;
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        *count = base_s;
-        if (count_out) *count_out = base_s;
-    }
-}
-
 __global__ void copy_f32_kernel(const float *src, float *dst) { *dst = *src; }
 
 void launch_copy_f32(const float *src, float *dst, hipStream_t stream) {
     copy_f32_kernel<<<dim3(1), dim3(1), 0, stream>>>(src, dst);
-}
-
-void launch_outlier_prep(const void *x, int64_t M, int64_t K, float threshold, float *colmax,
-                         float *mask, int32_t *idx, int32_t *count, int32_t *count_out,
-                         hipStream_t stream) {
-    launch_absmax(x, F16, M, K, 0, colmax, stream);
-    outlier_list_kernel<<<dim3(1), dim3(1024), 0, stream>>>(colmax, K, threshold, mask, idx,
-                                                            count, count_out);
 }
 
 }  // namespace sq

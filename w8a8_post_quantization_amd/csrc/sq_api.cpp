@@ -27,7 +27,8 @@ int finish() {
 inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct MixedWs {
-    size_t xq, xs, colmax, mask, idx, count, total;
+    size_t xq, xs, colmax, mask, idx, count, xo, wo, total;
+    int cap;  // outlier columns the compact side operands hold
 };
 
 // Device memory for sq_int8_mixed_matmul_noalloc: one array per GPU, held
@@ -60,8 +61,11 @@ void *scratch_ptr(int *err) {
     return scratch_dev[dev];
 }
 
-MixedWs mixed_layout(int64_t M, int64_t K) {
+static_assert(SQ_MIXED_SIDE_COLS <= sq::kSideColsMax, "side operand columns");
+
+MixedWs mixed_layout(int64_t M, int64_t N, int64_t K) {
     MixedWs w{};
+    w.cap = (int)(K < SQ_MIXED_SIDE_COLS ? K : SQ_MIXED_SIDE_COLS);
     size_t off = 0;
     w.xq = off; off += round256((size_t)M * (size_t)K);
     w.xs = off; off += round256((size_t)M * 4);
@@ -69,6 +73,8 @@ MixedWs mixed_layout(int64_t M, int64_t K) {
     w.mask = off; off += round256((size_t)K * 4);
     w.idx = off; off += round256((size_t)K * 4);
     w.count = off; off += 256;
+    w.xo = off; off += round256((size_t)w.cap * (size_t)M * 4);
+    w.wo = off; off += round256((size_t)w.cap * (size_t)N * 4);
     w.total = off;
     return w;
 }
@@ -294,9 +300,9 @@ int sq_norm_quantize_act(const void *x, int dt, int64_t M, int64_t K, int norm,
     return finish();
 }
 
-size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t K) {
-    if (M < 0 || K < 0) return 0;
-    return mixed_layout(M, K).total;
+size_t sq_int8_mixed_matmul_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return mixed_layout(M, N, K).total;
 }
 
 }  // extern "C"
@@ -308,17 +314,26 @@ namespace {
 int mixed_checked(const void *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
                   const void *w_f16, int64_t N, float threshold, char *ws, void *y, int y_dt,
                   int32_t *acc_out, int32_t *n_outliers_out, hipStream_t s, int tile) {
-    const MixedWs L = mixed_layout(M, K);
+    const MixedWs L = mixed_layout(M, N, K);
     auto *xq = reinterpret_cast<int8_t *>(ws + L.xq);
     auto *xs = reinterpret_cast<float *>(ws + L.xs);
     auto *colmax = reinterpret_cast<float *>(ws + L.colmax);
     auto *mask = reinterpret_cast<float *>(ws + L.mask);
     auto *idx = reinterpret_cast<int32_t *>(ws + L.idx);
     auto *count = reinterpret_cast<int32_t *>(ws + L.count);
-    sq::launch_outlier_prep(x, M, K, threshold, colmax, mask, idx, count, n_outliers_out, s);
-    sq::launch_quant_rows(x, SQ_F16, M, K, mask, 1, nullptr, xq, xs, s);
-    sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16), idx,
-                      count};
+    auto *xo = reinterpret_cast<float *>(ws + L.xo);
+    auto *wo = reinterpret_cast<float *>(ws + L.wo);
+    // column abs-max, then the masked row quantizer; extra blocks of that
+    // launch write the mask, the outlier list, |O| and (|O| <= cap) the
+    // outlier columns of x and w, gathered once for the GEMM's side term
+    sq::launch_absmax(x, SQ_F16, M, K, 0, colmax, s);
+    sq::OutlierList ol{};
+    ol.on = 1; ol.thr = threshold; ol.mask = mask; ol.idx = idx; ol.count = count;
+    ol.count_out = n_outliers_out; ol.w16 = static_cast<const uint16_t *>(w_f16);
+    ol.M = M; ol.N = N; ol.xo = xo; ol.wo = wo; ol.cap = L.cap;
+    sq::launch_quant_rows(x, SQ_F16, M, K, colmax, 1, nullptr, xq, xs, s, nullptr, &ol);
+    const sq::SideTerm side{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_f16),
+                            idx, count, xo, wo, L.cap};
     sq::launch_gemm(xq, wq, M, N, K, xs, 1, w_scale, y, y_dt, acc_out, &side, s, tile);
     return finish();
 }
@@ -359,7 +374,7 @@ int sq_int8_mixed_matmul_tile(const void *x, int64_t M, int64_t K, const int8_t 
     int st_ = mixed_args(x, M, K, wq, w_scale, w_f16, N, threshold, y, y_dt, acc_out,
                          n_outliers_out, &nothing);
     if (st_ != SQ_OK || nothing) return st_;
-    if (!workspace || workspace_bytes < mixed_layout(M, K).total) return SQ_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < mixed_layout(M, N, K).total) return SQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SQ_ERR_ALIGN;
     return mixed_checked(x, M, K, wq, w_scale, w_f16, N, threshold,
                          static_cast<char *>(workspace), y, y_dt, acc_out, n_outliers_out,
@@ -383,7 +398,7 @@ int sq_int8_mixed_matmul_noalloc(const void *x, int64_t M, int64_t K, const int8
     int st_ = mixed_args(x, M, K, wq, w_scale, w_f16, N, threshold, y, y_dt, acc_out,
                          n_outliers_out, &nothing);
     if (st_ != SQ_OK || nothing) return st_;
-    if (mixed_layout(M, K).total > (size_t)SQ_MIXED_SCRATCH_BYTES) return SQ_ERR_WORKSPACE;
+    if (mixed_layout(M, N, K).total > (size_t)SQ_MIXED_SCRATCH_BYTES) return SQ_ERR_WORKSPACE;
     int err = SQ_OK;
     void *ws = scratch_ptr(&err);
     if (!ws) return err;
