@@ -114,12 +114,10 @@ struct SideLds {
 // `compact` the values come from the gathered side operands (p.xo, p.wo:
 // one column's rows are contiguous, so a wave's load is coalesced); else
 // each is a 2-byte gather from the fp16 rows at the column's index (a
-// scalar load).  With `pre`, px and pw hold the compact values of the first
-// group of the first chunk, fetched by side_prefetch at kernel start.
+// scalar load).
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *wo, int m0,
-                                           int n0, int t0, int tn, bool compact, bool pre,
-                                           const float (&px)[4], const float (&pw)[4]) {
+                                           int n0, int t0, int tn, bool compact) {
     static_assert(BM % 64 == 0 && BN % 64 == 0 && NT % BM == 0 && NT % BN == 0,
                   "side staging");
     constexpr int PX = NT / BM, PW = NT / BN, G = 4;
@@ -137,13 +135,7 @@ __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *
     const int32_t *idx = p.idx + t0;
     for (int q = 0; q * G * PX < tn || q * G * PW < tn; ++q) {
         float vx[G], vw[G];
-        if (compact && pre && t0 == 0 && q == 0) {
-#pragma unroll
-            for (int k = 0; k < G; ++k) {
-                vx[k] = px[k];
-                vw[k] = pw[k];
-            }
-        } else if (compact) {
+        if (compact) {
 #pragma unroll
             for (int k = 0; k < G; ++k) {
                 const int t = cx + PX * (q * G + k);
@@ -177,29 +169,6 @@ __device__ __forceinline__ void stage_side(const GemmArgs &p, float *xo, float *
             if (t < tn) wo[t * WS + rw] = vw[k];
         }
     }
-}
-
-// The first group of stage_side's compact side values (columns
-// tid / BM + k NT / BM and tid / BN + k NT / BN, k < 4) read at kernel start,
-// before |O| is known: the compact arrays hold side_cap columns, so every
-// read is in bounds, and staging keeps only the columns below |O|.  Valid
-// (returns true) when p.xo is set and side_cap covers the group.
-template <int BM, int BN, int NT>
-__device__ __forceinline__ bool side_prefetch(const GemmArgs &p, int m0, int n0, float (&px)[4],
-                                              float (&pw)[4]) {
-    constexpr int PX = NT / BM, PW = NT / BN, G = 4;
-    constexpr int SPAN = (PX > PW ? PX : PW) * G;
-    if (!p.xo || p.side_cap < SPAN) return false;
-    const int tid = threadIdx.x;
-    const int mr = m0 + tid % BM < p.M ? m0 + tid % BM : p.M - 1;
-    const int nr = n0 + tid % BN < p.N ? n0 + tid % BN : p.N - 1;
-    const int cx = tid / BM, cw = tid / BN;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-        px[k] = p.xo[(int64_t)(cx + PX * k) * p.M + mr];
-        pw[k] = p.wo[(int64_t)(cw + PW * k) * p.N + nr];
-    }
-    return true;
 }
 
 // Each thread fetches (at most) one row step and one column step at kernel
@@ -273,8 +242,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p,
         for (int t0 = 0; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            const float none[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn, compact, false, none, none);
+            stage_side<BM, BN, 256>(p, xo, wo, m0, n0, t0, tn, compact);
             __syncthreads();
             // column by column, so each output still sums in ascending order
             for (int t = 0; t < tn; ++t) {
@@ -562,12 +530,92 @@ __device__ __forceinline__ void lds_barrier() {
 // holds output column n = 8*(v/4) + 4*(l/32) + (v%4) of n-fragment i and
 // row m = l%32 of m-fragment j: four consecutive columns of one row per
 // group of four registers.
+// Side sums over staged columns t_begin .. tn - 1 (column t of the activation
+// rows at xo[t * XS + r], of the weight rows at wo[t * WS + r]), column by
+// column, so that each output still sums in ascending column order; each
+// thread's outputs are its accumulator fragments' (32x32 layout).
+template <int BM, int BN, int WM, int WN, int XS, int WS>
+__device__ __forceinline__ void side_columns(const float *xo, const float *wo, int t_begin,
+                                             int tn,
+                                             float (&side)[BN / WN / 32][BM / WM / 32][16]) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int t = t_begin; t < tn; ++t) {
+        float xv[FM];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) xv[j] = xo[t * XS + wm * WTM + j * 32 + fr];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(wo + t * WS + wn * WTN +
+                                                                    i * 32 + 8 * g + 4 * fh);
+                const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        side[i][j][4 * g + q] = side_fma(xv[j], wq[q], side[i][j][4 * g + q]);
+            }
+    }
+}
+
+// The first side columns (at most kSideEarly, and at most one per main-loop
+// stage) are summed inside the main loop, one column per iteration, where
+// the vector ALUs are otherwise idle.  Their compact operands go straight
+// to an LDS area beside the ring with direct-to-LDS dword loads issued at
+// kernel start, before the ring's: loads complete in issue order, so the
+// ring's first wait covers them, and they hold no registers.  The area is
+// column-major like SideLds (activations ex[t XS + r], XS = BM + 4, then
+// weights ew[t WS + r], WS = BN + 4); a wave fills 64 consecutive rows of one
+// column per load.  The compact arrays hold side_cap >= kSideEarly columns
+// (else nothing is loaded here), so the loads are in bounds whatever |O| turns out to be; columns past |O| are
+// never read.  Returns false (nothing issued) without compact operands.
+constexpr int kSideEarly = 8;
+template <int BM, int BN, int NT>
+__device__ __forceinline__ bool side_early_load(const GemmArgs &p, int m0, int n0,
+                                                uint32_t area) {
+    constexpr int PX = NT / BM, PW = NT / BN, XS = BM + 4, WS = BN + 4;
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && kSideEarly % PX == 0 &&
+                  kSideEarly % PW == 0, "early side columns");
+    if (!p.xo || p.side_cap < kSideEarly) return false;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // activations: this wave's rows rb .. rb + 63 of column cx + PX k
+    const int rbx = (wave * 64) % BM, cx = (wave * 64) / BM;
+    const int mr = m0 + rbx + lane < p.M ? m0 + rbx + lane : p.M - 1;
+#pragma unroll
+    for (int k = 0; k < kSideEarly / PX; ++k) {
+        const int t = cx + PX * k;
+        const float *src = p.xo + (int64_t)t * p.M + mr;
+        const uint32_t dst = area + (uint32_t)((t * XS + rbx) * 4);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                     : : "v"(src), "s"(dst) : "memory", "m0");
+    }
+    const int rbw = (wave * 64) % BN, cw = (wave * 64) / BN;
+    const int nr = n0 + rbw + lane < p.N ? n0 + rbw + lane : p.N - 1;
+#pragma unroll
+    for (int k = 0; k < kSideEarly / PW; ++k) {
+        const int t = cw + PW * k;
+        const float *src = p.wo + (int64_t)t * p.N + nr;
+        const uint32_t dst = area + (uint32_t)((kSideEarly * XS + t * WS + rbw) * 4);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                     : : "v"(src), "s"(dst) : "memory", "m0");
+    }
+    return true;
+}
+
 template <int BM, int BN, int WM, int WN, int YDT, bool SIDE, typename AccV>
 __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
                                             AccV (&acc)[BN / WN / 32][BM / WM / 32],
                                             int8_t *smem, const float *sx, const float *sw,
-                                            int m0, int n0, bool pre,
-                                            const float (&px)[4], const float (&pw)[4]) {
+                                            int m0, int n0, int cnt_in,
+                                            float (&side)[SIDE ? BN / WN / 32 : 1]
+                                                         [SIDE ? BM / WM / 32 : 1][16],
+                                            int t_from) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int NT = 64 * WM * WN;
@@ -575,45 +623,21 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
     const int wm = wave / WN, wn = wave % WN;
     const int fr = lane & 31, fh = lane >> 5;
     const int M = p.M, N = p.N;
-    float side[SIDE ? FN : 1][SIDE ? FM : 1][16];
     if constexpr (SIDE) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) side[i][j][v] = 0.0f;
+        // side holds the sums over the columns before t_from (added while
+        // the main loop's first stages loaded); the rest follow in order.
         using L = SideLds<BM, BN>;
         static_assert(L::BYTES <= 2 * (BM + BN) * 128, "side chunk fits the ring");
         float *xo = reinterpret_cast<float *>(smem);
         float *wo = xo + 32 * L::XS;
-        const int cnt = *p.count;
+        const int cnt = cnt_in;
         const bool compact = cnt <= p.side_cap;
-        for (int t0 = 0; t0 < cnt; t0 += 32) {
+        for (int t0 = t_from; t0 < cnt; t0 += 32) {
             const int tn = cnt - t0 < 32 ? cnt - t0 : 32;
             __syncthreads();
-            stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn, compact, pre, px, pw);
+            stage_side<BM, BN, NT>(p, xo, wo, m0, n0, t0, tn, compact);
             __syncthreads();
-            // column by column, so each output still sums in ascending order
-            for (int t = 0; t < tn; ++t) {
-                float xv[FM];
-#pragma unroll
-                for (int j = 0; j < FM; ++j) xv[j] = xo[t * L::XS + wm * WTM + j * 32 + fr];
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const float4 w4 = *reinterpret_cast<const float4 *>(
-                            wo + t * L::WS + wn * WTN + i * 32 + 8 * g + 4 * fh);
-                        const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                        for (int j = 0; j < FM; ++j)
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                side[i][j][4 * g + q] = side_fma(xv[j], wq[q], side[i][j][4 * g + q]);
-                            }
-                    }
-            }
+            side_columns<BM, BN, WM, WN, L::XS, L::WS>(xo, wo, 0, tn, side);
         }
     }
     // Exact int32 sums, when asked for (direct stores, not on the fast path).
@@ -788,6 +812,8 @@ gemm_pp(GemmArgs p) {
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[STA * SA + STB * SB];
     __shared__ __attribute__((aligned(16))) float sx[BM], sw[BN];
+    // the early side columns' operands (side_early), beside the ring
+    __shared__ __attribute__((aligned(16))) float sside[SIDE ? kSideEarly * (BM + BN + 8) : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -797,11 +823,20 @@ gemm_pp(GemmArgs p) {
     const int M = p.M, N = p.N, K = p.K;
     TileScales<BM, BN> scl;
     scl.load(p, m0, n0);
-    // LLM.int8(): the side term's first operand group, fetched now so its
-    // latency hides under the main loop instead of following it.
-    float spx[4] = {0.0f, 0.0f, 0.0f, 0.0f}, spw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    bool spre = false;
-    if constexpr (SIDE) spre = side_prefetch<BM, BN, 64 * NW>(p, m0, n0, spx, spw);
+    // LLM.int8(): |O| read now, so nothing waits for it later; the side
+    // sums (side_early_load, side_columns) start from zero.
+    int scnt = 0;
+    float side[SIDE ? FN : 1][SIDE ? FM : 1][16];
+    int t_from = 0;  // side columns summed before the epilogue
+    if constexpr (SIDE) {
+        scnt = *p.count;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) side[i][j][v] = 0.0f;
+    }
 
     const int8_t *a_src[LA];
     const int8_t *b_src[LB];
@@ -919,7 +954,8 @@ gemm_pp(GemmArgs p) {
         wait_vmcnt<0>();
         scl.publish(sx, sw);
         __syncthreads();
-        epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, spre, spx, spw);
+        epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, scnt, side,
+                                              t_from);
         return;
     } else {
     // Main loop.  Its two halves are branch-free so the scheduler can
@@ -933,16 +969,30 @@ gemm_pp(GemmArgs p) {
     constexpr int RQ = FM + FN;  // ds_read_b128 per quarter
     constexpr int MQ = FM * FN;  // MFMAs per quarter
     static_assert(RQ <= MQ, "one read per MFMA slot");
+    bool searly = false;  // the early side operands were loaded
+    if constexpr (SIDE)
+        searly = side_early_load<BM, BN, 64 * NW>(p, m0, n0,
+                                                  (uint32_t)(uintptr_t)(lds_void_t *)sside);
 #pragma unroll
     for (int s = 0; s < STA; ++s) {
         issue_a(s);
         issue_b(s);
     }
+    // side columns summed in the main loop (kSideEarly at most, one per
+    // stage; compact operands only)
+    int te = 0;
+    if constexpr (SIDE) {
+        if (searly && scnt > 0 && scnt <= p.side_cap) {
+            te = scnt < kSideEarly ? scnt : kSideEarly;
+            te = te < nk ? te : nk;
+        }
+        t_from = te;
+    }
     wait_vmcnt<(STA - 1) * L>();
     lds_barrier();
     int4v xa[FM], wa[FN], xb[FM], wb[FN];
     read_frags(0, 0, xa, wa);
-    for (int kt = 0; kt < nk; ++kt) {
+    auto step = [&](int kt) {
         read_frags(kt, 1, xb, wb);
         mma(xa, wa);
         read_frags(kt, 2, xa, wa);
@@ -965,11 +1015,23 @@ gemm_pp(GemmArgs p) {
         issue_b(kt + STB);
         mma(xb, wb);
         sched_tail<MQ, RQ, L, 0>();  // MFMA, DS read, direct loads, ...
+    };
+    int kt = 0;
+    if constexpr (SIDE) {
+        // the first te stages each add one early side column (a loop of its
+        // own, so the main loop below is the plain one)
+        for (; kt < te; ++kt) {
+            step(kt);
+            side_columns<BM, BN, WM, WN, BM + 4, BN + 4>(sside, sside + kSideEarly * (BM + 4), kt,
+                                                         kt + 1, side);
+        }
     }
+    for (; kt < nk; ++kt) step(kt);
     wait_vmcnt<0>();
     scl.publish(sx, sw);
     __syncthreads();  // steps visible; the side term may reuse the ring
-    epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, spre, spx, spw);
+    epilogue_nt<BM, BN, WM, WN, YDT, SIDE>(p, acc, smem, sx, sw, m0, n0, scnt, side,
+                                              t_from);
     }
 }
 
