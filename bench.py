@@ -502,6 +502,17 @@ def extras(torch, L, _sp, T, chk):
     us_w = _time_loop(torch, fns[:1], 30)
     res["gemm_prefill_warm"] = {"us": round(us_w, 2),
                                 "TOPS": round(2.0 * M * N * K / us_w / 1e6, 1)}
+    # Context, not a target: the vendor int8 GEMM (torch._int_mm, hipBLASLt;
+    # int32 out, no dequant epilogue) on the same operands, cold and warm.
+    vendor = {}
+    try:
+        fns_v = [lambda w=w: torch._int_mm(xq, w.t()) for w in wqs]
+        for name, f in (("cold", fns_v), ("warm", fns_v[:1])):
+            us_v = _time_loop(torch, f, 20)
+            vendor[name] = {"us": round(us_v, 2), "TOPS": round(2.0 * M * N * K / us_v / 1e6, 1)}
+    except RuntimeError as e:  # not every build ships the int8 path
+        vendor = {"error": str(e)[:120]}
+    res["vendor_int8_mm_prefill"] = vendor
     del wqs
 
     # The same prefill GEMM on the e4m3 path (finite codes: NaN codes never

@@ -120,6 +120,7 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
     __shared__ int64_t sh_s1[2][4];
     __shared__ int64_t sh_lo[2][4], sh_hi[2][4];
     __shared__ float sh_max[2][4];
+    __shared__ float sh_stat[2][2];  // mu, rstd of the row (written by wave 0)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // wave-uniform
     if (!DYN && blockIdx.x == 0 && tid == 0) scale[0] = static_scale[0];
@@ -203,17 +204,27 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const uint4 *__restrict
         }
         __syncthreads();
         // Row totals: |S1| < 2^54, H < 2^53, |L| < 2^54; the row's
-        // sum (x 2^24)^2 = H 2^41 + L.
-        int64_t S1 = 0, H = 0, L = 0;
+        // sum (x 2^24)^2 = H 2^41 + L.  Wave 0 alone turns them into mu and
+        // rstd (about a tenth of a row's VALU work per wave, in fp64
+        // divisions and a square root) and passes them on through LDS.
+        if (wave_base == 0) {
+            int64_t S1 = 0, H = 0, L = 0;
     #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if constexpr (NORM == 0) S1 += sh_s1[PAR][w];
-            H += sh_hi[PAR][w];
-            L += sh_lo[PAR][w];
+            for (int w = 0; w < 4; ++w) {
+                if constexpr (NORM == 0) S1 += sh_s1[PAR][w];
+                H += sh_hi[PAR][w];
+                L += sh_lo[PAR][w];
+            }
+            const u128 S2 = (u128)(((__int128)H << 41) + L);
+            float mu0, rstd0;
+            norm_stats<NORM>(S1, S2, K, eps, mu0, rstd0);
+            if (lane == 0) {
+                sh_stat[PAR][0] = mu0;
+                sh_stat[PAR][1] = rstd0;
+            }
         }
-        const u128 S2 = (u128)(((__int128)H << 41) + L);
-        float mu, rstd;
-        norm_stats<NORM>(S1, S2, K, eps, mu, rstd);
+        __syncthreads();
+        const float mu = sh_stat[PAR][0], rstd = sh_stat[PAR][1];
 
         // The normalized, scaled row (kept in registers for the store pass).
         // Slots past the row's end hold copies of its last vector (clamped
