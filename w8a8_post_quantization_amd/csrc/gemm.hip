@@ -1334,7 +1334,12 @@ static bool dec_rows_112(int64_t N) {
 // how much MFMA work each tile does per byte staged through LDS.
 static int pick_tile(int64_t M, int64_t N, int64_t K) {
     struct C { int bm, bn; double eff; int per_cu; };
-    const C cands[3] = {{256, 256, 1.0, 1}, {256, 128, 0.85, 1}, {128, 128, 0.7, 2}};
+    // 256 x 128 relative to 256 x 256: 0.85 per unit of work at long K, 0.72
+    // at K <= 2048, where each tile's prologue and epilogue weigh more
+    // (4096 x 4096 x 1024: one round of 256 x 256 tiles 24.2 us, two of
+    // 256 x 128 33.4 us; 4096 x 6144 x 1024: 38.8 us against 45.0).
+    const double eff1 = K <= 2048 ? 0.72 : 0.85;
+    const C cands[3] = {{256, 256, 1.0, 1}, {256, 128, eff1, 1}, {128, 128, 0.7, 2}};
     int best = 0;
     double best_score = -1;
     for (int i = 0; i < 3; ++i) {
