@@ -45,6 +45,48 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "W8A8 GEMM TOPS + % INT8 MFMA peak (prefill); decode GB/s as % of HBM peak"
 
 
+def profile_streams():
+    """The activation-stream kernels of the extras (X fp16 [65536, 7168], 940
+    MB) launched eagerly 3 times each: column abs-max, the per-token
+    quantizer with 1/s, and the fused LayerNorm (with beta) -> per-token
+    int8, so that a counter run sees one dispatch per launch."""
+    import torch
+
+    import w8a8_post_quantization_amd as sq
+
+    L = sq.lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: t.data_ptr()  # noqa: E731
+    U = lambda n, scale: torch.rand(n, generator=g, device=dev) * scale + scale * 0.1  # noqa: E731
+
+    def chk(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {L.sq_status_str(rc).decode()}")
+
+    M, K = 65536, 7168
+    X = torch.randn((M, K), dtype=torch.float16, generator=g, device=dev)
+    X[:, :6] *= 50.0
+    inv, gam, bet = U(K, 1.0), U(K, 1.0), U(K, 0.1)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    am = torch.empty(K, dtype=torch.float32, device=dev)
+    ran = []
+    for name, fn in (
+            ("absmax", lambda: chk(L.sq_absmax_reduce(P(X), 1, M, K, 0, P(am), sp), "absmax")),
+            ("quantize", lambda: chk(L.sq_quantize_act(P(X), 1, M, K, P(inv), 1, None, P(xq),
+                                                       P(xs), sp), "quantize")),
+            ("norm_quantize", lambda: chk(L.sq_norm_quantize_act(P(X), 1, M, K, 0, P(gam), P(bet),
+                                                                 1e-5, 1, None, P(xq), P(xs),
+                                                                 sp), "norm"))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ran.append(name)
+    print(json.dumps({"profile_streams": ran}), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +104,10 @@ def parse():
     ap.add_argument("--profile-gemms", action="store_true",
                     help="only run the GEMM workloads eagerly, a few launches each, for "
                          "rocprofv3 counter runs (MFMA utilisation, HBM bytes)")
+    ap.add_argument("--profile-streams", action="store_true",
+                    help="only run the 940 MB activation-stream kernels (abs-max, per-token "
+                         "quantizer, fused norm -> int8) eagerly, 3 launches each, for "
+                         "rocprofv3 counter runs")
     return ap.parse_args()
 
 
@@ -213,6 +259,9 @@ def main():
         return
     if args.profile_gemms:
         profile_gemms()
+        return
+    if args.profile_streams:
+        profile_streams()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
