@@ -274,7 +274,7 @@ int sq_int8_mixed_matmul(const void *x, int64_t M, int64_t K, const int8_t *wq,
  * runs on until the process ends; the call allocates nothing.
  *   Returns SQ_ERR_WORKSPACE when sq_int8_mixed_matmul_workspace(M, N, K)
  *   exceeds SQ_MIXED_SCRATCH_BYTES (M = 2048, N = K = 4096 needs about
- *   11.6 MB; with N = K = 4096 up to about 6500 rows fit),
+ *   11.6 MB; with N = K = 4096 up to 6810 rows fit),
  *   SQ_ERR_HIP when the array's device address cannot be obtained (looked up
  *   once per GPU, with that GPU current, on the first call there).
  * Every call on a GPU uses that GPU's one array: calls that overlap on one
