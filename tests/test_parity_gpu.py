@@ -213,7 +213,10 @@ def test_gemm_extremal_values(torch):
     (300, 200, 512, 6.0, None, 128), (300, 200, 512, 6.0, None, 129),
     (260, 136, 384, 6.0, "2", 129),
     # the outlier list over more than one 4096-column pass
-    (64, 96, 8208, 6.0, None, 40), (300, 200, 4112, 6.0, None, 6), (2048, 64, 12288, 6.0, None, 24)])
+    (64, 96, 8208, 6.0, None, 40), (300, 200, 4112, 6.0, None, 6), (2048, 64, 12288, 6.0, None, 24),
+    # rows longer than the 16384 multipliers staged in LDS: the mask read
+    # from the column maxima in global memory
+    (40, 64, 16512, 6.0, None, 12), (300, 100, 16400, 6.0, None, 7)])
 def test_mixed_parity(torch, M, N, K, thr, tile, n_dims):
     import synth
 
