@@ -41,6 +41,21 @@ int sq_int8_mixed_matmul_tile(const void *x, int64_t M, int64_t K, const int8_t 
                               int y_dt, int32_t *acc_out, int32_t *n_outliers_out, void *stream,
                               int tile);
 
+/*
+ * The fused norm -> int8 quantizer of sq.h with its kernel forced:
+ *   kernel  -1 the library's choice; 0 the block-per-row kernel; 1 the
+ *           wave-per-row kernel (built for K = 2048, 3072, ..., 8192; other
+ *           K run the block-per-row kernel).  Other values return
+ *           SQ_ERR_ARG.  Both kernels give the same bits (exact row sums,
+ *           the same per-element operations).
+ * Defined by the passage of its sq.h counterpart: the SmoothQuant tutorial
+ * page's section on folding the smoothing into LayerNorm.
+ */
+int sq_norm_quantize_act_kernel(const void *x, int dt, int64_t M, int64_t K, int norm,
+                                const float *gamma, const float *beta, float eps, int mode,
+                                const float *static_scale, int8_t *xq, float *x_scale,
+                                void *stream, int kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     assert L.sq_version() == 103
     test_only = sq.header_functions(sq.TEST_HEADER)
     assert test_only == ["sq_gemm_fp8_dequant_tile", "sq_gemm_i8_dequant_tile",
-                         "sq_int8_mixed_matmul_tile"]
+                         "sq_int8_mixed_matmul_tile", "sq_norm_quantize_act_kernel"]
     for name in test_only:
         assert hasattr(L, name) and name in sq.SIGNATURES, name
 
@@ -39,8 +39,12 @@ def test_forced_tile_is_checked():
                                           sq.SQ_F32, None, bad) == ARG
         assert L.sq_int8_mixed_matmul_tile(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 6.0, FAKE, 1 << 20,
                                            FAKE, sq.SQ_F16, None, None, None, bad) == ARG
+        assert L.sq_norm_quantize_act_kernel(FAKE, sq.SQ_F16, 64, 512, 0, FAKE, None, 1e-5, 1,
+                                             None, FAKE, FAKE, None, bad) == ARG
     assert L.sq_gemm_i8_dequant_tile(FAKE, FAKE, 64, 64, 40, FAKE, 1, FAKE, FAKE, sq.SQ_F32,
                                      None, None, 1) == SHAPE
+    assert L.sq_norm_quantize_act_kernel(FAKE, sq.SQ_F16, 64, 40, 0, FAKE, None, 1e-5, 1,
+                                         None, FAKE, FAKE, None, 1) == SHAPE
 
 
 def test_status_strings():

@@ -207,7 +207,7 @@ def test_activation_stream(torch):
     assert_bits_equal(host(xs8, torch), xs8_o, "x_scale e4m3")
     assert_bits_equal(host(xq8, torch), xq8_o, "xq e4m3")
     # the fused LayerNorm -> int8 (beta, per token) the benchmark times on
-    # this stream: 65536 rows, 32 per block, beta staged in LDS
+    # this stream: 65536 rows, one wave per row, gamma and beta in LDS
     log("stream fused norm -> int8")
     g, b = synth.norm_params(X.shape[1])
     xqn, xsn = sq.norm_quantize_act(dev(X, torch), dev(g, torch), dev(b, torch),

@@ -75,6 +75,63 @@ def test_norm_quantize_parity(torch, M, K, norm, with_beta, mode):
     assert_bits_equal(host(xq, torch), xq_o, "xq")
 
 
+@pytest.mark.parametrize("M,K,norm,with_beta,mode", [
+    # the wave-per-row kernel forced, at every row length it is built for
+    # (K = 2048, 3072, ..., 8192), with rows fewer than, equal to and more
+    # than its waves, ragged over them
+    (1, 2048, 0, True, 1), (9, 3072, 1, False, 1), (37, 4096, 0, True, 0),
+    (300, 5120, 1, True, 1), (2049, 6144, 0, True, 1), (100, 7168, 0, False, 0),
+    (513, 8192, 1, True, 1), (4099, 7168, 0, True, 1), (2053, 7168, 1, False, 0),
+    (77, 2048, 0, True, 1), (3001, 8192, 1, True, 1), (2048, 4096, 0, False, 0)])
+def test_norm_quantize_wave_kernel(torch, M, K, norm, with_beta, mode):
+    x = _x(M * 17 + K, M, K)
+    g, b = synth.norm_params(K, seed=M + 2 * K)
+    b = b if with_beta else None
+    st = np.array([0.01, 100.0], np.float32) if mode == 0 else None
+    eps = 1e-5 if norm == 0 else 1e-6
+    log(f"norm_quantize wave kernel M={M} K={K} norm={norm} beta={with_beta} mode={mode}")
+    xq, xs = sq.norm_quantize_act(dev(x, torch), dev(g, torch),
+                                  None if b is None else dev(b, torch), norm, eps, mode,
+                                  None if st is None else dev(st, torch), kernel=1)
+    xq_o, xs_o = oracle.norm_quantize(x, g, b, norm, eps, mode, st)
+    assert_bits_equal(host(xs, torch), xs_o, "x_scale")
+    assert_bits_equal(host(xq, torch), xq_o, "xq")
+
+
+def test_norm_quantize_kernels_agree_many_rows(torch):
+    """At 8200 rows x 7168 the library picks the wave-per-row kernel; the
+    block-per-row kernel forced on the same rows gives the same bits, and
+    both match the oracle on every row."""
+    M, K = 8200, 7168
+    x = _x(5, M, K)
+    g, b = synth.norm_params(K, seed=3)
+    xd, gd, bd = dev(x, torch), dev(g, torch), dev(b, torch)
+    xq_o, xs_o = oracle.norm_quantize(x, g, b, 0, 1e-5)
+    for kernel in (None, 0, 1):
+        log(f"norm_quantize {M}x{K} kernel={kernel}")
+        xq, xs = sq.norm_quantize_act(xd, gd, bd, 0, 1e-5, kernel=kernel)
+        assert_bits_equal(host(xs, torch), xs_o, f"x_scale kernel={kernel}")
+        assert_bits_equal(host(xq, torch), xq_o, f"xq kernel={kernel}")
+
+
+@pytest.mark.parametrize("norm,with_beta,mode", [(1, False, 0), (0, True, 0), (1, True, 1)])
+def test_norm_quantize_wave_kernel_streamed_codes(torch, norm, with_beta, mode):
+    """Codes beyond the 256 MB last-level cache are stored nontemporally:
+    33000 rows x 8192 (270 MB of codes) through that store path."""
+    M, K = 33000, 8192
+    x = _x(101 + norm, M, K)
+    g, b = synth.norm_params(K, seed=13)
+    b = b if with_beta else None
+    st = np.array([0.02, 50.0], np.float32) if mode == 0 else None
+    log(f"norm_quantize streamed codes M={M} K={K} norm={norm} beta={with_beta} mode={mode}")
+    xq, xs = sq.norm_quantize_act(dev(x, torch), dev(g, torch),
+                                  None if b is None else dev(b, torch), norm, 1e-5, mode,
+                                  None if st is None else dev(st, torch))
+    xq_o, xs_o = oracle.norm_quantize(x, g, b, norm, 1e-5, mode, st)
+    assert_bits_equal(host(xs, torch), xs_o, "x_scale")
+    assert_bits_equal(host(xq, torch), xq_o, "xq")
+
+
 def test_norm_quantize_extreme_rows(torch):
     """Largest fp16 magnitudes, subnormals, constant and zero rows."""
     K = 4096
@@ -88,11 +145,13 @@ def test_norm_quantize_extreme_rows(torch):
     x[5, 7] = np.float16(3.0)
     g, b = synth.norm_params(K, seed=11)
     for norm in (0, 1):
-        log(f"norm_quantize extremes norm={norm}")
-        xq, xs = sq.norm_quantize_act(dev(x, torch), dev(g, torch), dev(b, torch), norm, 1e-5)
         xq_o, xs_o = oracle.norm_quantize(x, g, b, norm, 1e-5)
-        assert_bits_equal(host(xs, torch), xs_o, "x_scale")
-        assert_bits_equal(host(xq, torch), xq_o, "xq")
+        for kernel in (0, 1):
+            log(f"norm_quantize extremes norm={norm} kernel={kernel}")
+            xq, xs = sq.norm_quantize_act(dev(x, torch), dev(g, torch), dev(b, torch), norm,
+                                          1e-5, kernel=kernel)
+            assert_bits_equal(host(xs, torch), xs_o, "x_scale")
+            assert_bits_equal(host(xq, torch), xq_o, "xq")
 
 
 def test_folded_norm_prefill_full_size(torch):

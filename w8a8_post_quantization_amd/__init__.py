@@ -55,6 +55,8 @@ SIGNATURES = {
                                           _P]),
     "sq_fold_norm": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "sq_norm_quantize_act": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P]),
+    "sq_norm_quantize_act_kernel": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _F, _I, _P, _P, _P, _P,
+                                         _I]),
     "sq_static_scale": (_I, [_P, _P, _I64, _F, _P, _P]),
     "sq_smooth_weights_fp8": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P]),
     "sq_quantize_act_fp8": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _P]),
@@ -333,8 +335,11 @@ def fold_norm(gamma, s, beta=None, stream=None):
 
 
 def norm_quantize_act(x, gamma, beta=None, norm=SQ_NORM_LAYER, eps=1e-5,
-                      mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, out=None, stream=None):
-    """Fused fp16 norm -> int8: (xq int8 [M,K], x_scale fp32 [M] or [1])."""
+                      mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, out=None, stream=None,
+                      kernel=None):
+    """Fused fp16 norm -> int8: (xq int8 [M,K], x_scale fp32 [M] or [1]).
+    kernel (tests only): 0 or 1 forces the block- or wave-per-row kernel
+    through the coverage entry point of sq_test.h."""
     torch = _torch()
     x2 = x.reshape(-1, x.shape[-1])
     _check(x2, "x", (torch.float16,))
@@ -350,9 +355,12 @@ def norm_quantize_act(x, gamma, beta=None, norm=SQ_NORM_LAYER, eps=1e-5,
                          device=x.device)
     else:
         xq, xs = out
-    _call("sq_norm_quantize_act", x2.data_ptr(), _dt(x2), M, K, int(norm), gamma.data_ptr(),
-          _ptr(beta), float(eps), int(mode), _ptr(static_scale), xq.data_ptr(), xs.data_ptr(),
-          _stream(stream))
+    args = (x2.data_ptr(), _dt(x2), M, K, int(norm), gamma.data_ptr(), _ptr(beta), float(eps),
+            int(mode), _ptr(static_scale), xq.data_ptr(), xs.data_ptr(), _stream(stream))
+    if kernel is None:
+        _call("sq_norm_quantize_act", *args)
+    else:
+        _call("sq_norm_quantize_act_kernel", *args, int(kernel))
     return xq, xs
 
 

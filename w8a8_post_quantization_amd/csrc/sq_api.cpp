@@ -277,6 +277,15 @@ int sq_fold_norm(const float *gamma, const float *beta, const float *s, int64_t 
 int sq_norm_quantize_act(const void *x, int dt, int64_t M, int64_t K, int norm,
                          const float *gamma, const float *beta, float eps, int mode,
                          const float *static_scale, int8_t *xq, float *x_scale, void *stream) {
+    return sq_norm_quantize_act_kernel(x, dt, M, K, norm, gamma, beta, eps, mode, static_scale,
+                                       xq, x_scale, stream, -1);
+}
+
+int sq_norm_quantize_act_kernel(const void *x, int dt, int64_t M, int64_t K, int norm,
+                                const float *gamma, const float *beta, float eps, int mode,
+                                const float *static_scale, int8_t *xq, float *x_scale,
+                                void *stream, int kernel) {
+    if (kernel < -1 || kernel > 1) return SQ_ERR_ARG;
     if (dt != SQ_F16) return SQ_ERR_DTYPE;
     if (norm != SQ_NORM_LAYER && norm != SQ_NORM_RMS) return SQ_ERR_ARG;
     if (mode != SQ_PER_TENSOR_STATIC && mode != SQ_PER_TOKEN_DYNAMIC) return SQ_ERR_ARG;
@@ -296,7 +305,7 @@ int sq_norm_quantize_act(const void *x, int dt, int64_t M, int64_t K, int norm,
         !aligned(x_scale, 4) || !aligned(static_scale, 4))
         return SQ_ERR_ALIGN;
     sq::launch_norm_quant(x, M, K, norm, gamma, beta, eps, mode == SQ_PER_TOKEN_DYNAMIC,
-                          static_scale, xq, x_scale, st(stream));
+                          static_scale, xq, x_scale, st(stream), kernel);
     return finish();
 }
 
