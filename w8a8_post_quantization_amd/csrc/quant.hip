@@ -284,7 +284,7 @@ constexpr int kMulLds = 16384;
 // which would serialize the row's loads.  ITS = 0: rows longer than
 // 16 x 64 vectors, streamed twice (the second pass hits L2).
 template <int DT, bool HAS_MUL, bool DYN, int ITS, bool MUL_LDS, bool HAS_ROW, bool FP8,
-          bool NTS>
+          bool NTS, bool NTL>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict__ x,
                                                          int64_t rows, int64_t K,
                                                          const float *__restrict__ mul_g,
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4 *__restrict
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
                 const int64_t vi = lane + (int64_t)it * kWave;
-                b[it] = ld_nt(xr + (vi < nvec ? vi : nvec - 1));
+                b[it] = ld16<NTL>(xr + (vi < nvec ? vi : nvec - 1));
             }
         };
         auto finish_row = [&](int64_t r, const uint4 (&b)[ITS]) {
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256) void quant_row_block_kernel(const uint4 *__res
     for (int it = 0; it < ITS; ++it) {
         const int64_t vi = tid + (int64_t)it * 256;
         const int64_t vc = vi < nvec ? vi : nvec - 1;
-        raw[it] = ld_nt(xr + vc);
+        raw[it] = ld16<false>(xr + vc);  // at most 2048 rows: an input that may be read again
         if constexpr (HAS_MUL) load_mul<DT>(mul, vc * V, m[it]);
     }
     if constexpr (HAS_MUL) {
@@ -574,15 +574,21 @@ static void launch_q(const void *x, int64_t rows, int64_t K, const float *mul,
     dim3 grid((unsigned)(blocks + extra)), block(256);
     const int64_t nit = (nvec + kWave - 1) / kWave;  // vectors per lane
     const int its = !DYN ? 0 : nit <= 2 ? 2 : nit <= 4 ? 4 : nit <= 8 ? 8 : nit <= 16 ? 16 : 0;
-#define SQ_Q(ITS, LDS, NT)                                                                      \
-    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8, NT><<<grid, block, shmem, stream>>>( \
+    // Inputs larger than the caches are loaded nontemporally (codes
+    // beyond the cache imply such an input).
+    const bool ntl = nts || rows * K * dt_bytes(DT) > kNtLoadBytes;
+#define SQ_Q(ITS, LDS, NT, NL)                                                                  \
+    quant_rows_kernel<DT, HAS_MUL, DYN, ITS, LDS, HAS_ROW, FP8, NT, NL><<<grid, block, shmem,      \
+                                                                          stream>>>(            \
         xv, rows, K, mul, row_mul, static_scale, q, scale, (int)rpw, ol)
-#define SQ_QL(ITS)                                    \
-    do {                                              \
-        if (mul_lds && nts) SQ_Q(ITS, true, true);    \
-        else if (mul_lds) SQ_Q(ITS, true, false);     \
-        else if (nts) SQ_Q(ITS, false, true);         \
-        else SQ_Q(ITS, false, false);                 \
+#define SQ_QL(ITS)                                           \
+    do {                                                     \
+        if (mul_lds && nts) SQ_Q(ITS, true, true, true);     \
+        else if (mul_lds && ntl) SQ_Q(ITS, true, false, true); \
+        else if (mul_lds) SQ_Q(ITS, true, false, false);     \
+        else if (nts) SQ_Q(ITS, false, true, true);          \
+        else if (ntl) SQ_Q(ITS, false, false, true);         \
+        else SQ_Q(ITS, false, false, false);                 \
     } while (0)
     switch (its) {
         case 2: SQ_QL(2); break;

@@ -17,8 +17,9 @@ typedef int int16v __attribute__((ext_vector_type(16)));
 
 enum Dt { F32 = 0, F16 = 1, BF16 = 2 };
 
-// Element count of one 16-byte vector of each type.
+// Element count of one 16-byte vector of each type, and bytes per element.
 template <int DT> struct Vec { static constexpr int n = DT == F32 ? 4 : 8; };
+constexpr int dt_bytes(int dt) { return dt == F32 ? 4 : 2; }
 
 // Widen the elements of one 16-byte vector to fp32 (exact for all types).
 template <int DT>
@@ -50,6 +51,18 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
     const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// A 16-byte load of an input that is read once (NTL: nontemporal, for
+// inputs larger than the caches) or that the next kernel reads again (a
+// plain load, so it stays cached: LLM.int8() reads X in its outlier
+// detection and again in its quantizer).  Inputs above this many bytes
+// take the nontemporal form.
+constexpr int64_t kNtLoadBytes = (int64_t)64 << 20;
+template <bool NTL>
+__device__ __forceinline__ uint4 ld16(const uint4 *p) {
+    if constexpr (NTL) return ld_nt(p);
+    else return *p;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
