@@ -10,7 +10,9 @@
  * sq.h entry point of the same name, plus:
  *   tile  -1 the library's choice; 0, 1, 2 the block shapes 256 x 256,
  *         256 x 128, 128 x 128 (for M > 32; with M <= 32 the decode kernel
- *         runs either way).  Other values return SQ_ERR_ARG.
+ *         runs either way); for sq_gemm_i8_dequant_tile also 3, 128 x 128
+ *         tiles of eight waves in K-split pairs (K % 128 == 0; other K run
+ *         the 256 x 128 shape).  Other values return SQ_ERR_ARG.
  * Defined by the same passages as their sq.h counterparts: the SmoothQuant
  * tutorial page's Y = diag(dX) X_int8 W_int8 diag(dW); the LLM.int8()
  * explainer's §2.1 (int32 sums, outer-product dequant) and §2.2

@@ -58,7 +58,8 @@ def _stream(torch):
     (1, 37, 144, None, sq.SQ_F16), (7, 129, 1040, None, sq.SQ_F32), (17, 300, 256, None, sq.SQ_BF16),
     (32, 113, 4096, None, sq.SQ_F16), (33, 127, 128, 0, sq.SQ_F32), (257, 129, 1024, 0, sq.SQ_F16),
     (200, 300, 2048, 1, sq.SQ_BF16), (255, 257, 144, 1, sq.SQ_F32), (129, 131, 512, 2, sq.SQ_F16),
-    (300, 70, 1040, 2, sq.SQ_BF16)])
+    (300, 70, 1040, 2, sq.SQ_BF16), (129, 131, 512, 3, sq.SQ_F16), (300, 70, 2304, 3, sq.SQ_BF16),
+    (257, 255, 1040, 3, sq.SQ_F32)])
 def test_gemm_guards(torch, M, N, K, tile, ydt):
     L = sq.lib()
     rng = np.random.default_rng(M * 7 + N + K)

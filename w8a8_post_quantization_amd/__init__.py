@@ -218,8 +218,8 @@ def quantize_act(x, inv_s=None, mode=SQ_PER_TOKEN_DYNAMIC, static_scale=None, ou
 
 def gemm_i8_dequant(xq, wq, x_scale, w_scale, out_dtype=None, with_acc=False, out=None,
                     stream=None, tile=None):
-    """a5: y [M,N] (and acc int32 [M,N] if with_acc).  tile 0 | 1 | 2 forces
-    the tiled kernel's block shape (include/sq_test.h; same bits)."""
+    """a5: y [M,N] (and acc int32 [M,N] if with_acc).  tile 0 | 1 | 2 | 3
+    forces the tiled kernel's block shape (include/sq_test.h; same bits)."""
     torch = _torch()
     _check(xq, "xq", (torch.int8,), 2)
     _check(wq, "wq", (torch.int8,), 2)

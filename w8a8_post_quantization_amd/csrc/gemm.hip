@@ -1035,6 +1035,178 @@ gemm_pp(GemmArgs p) {
     }
 }
 
+// gemm_pp's tiles with eight waves in four pairs whose two waves split
+// every stage's K (int8, no side term).  A pair covers one (BM/2) x (BN/2)
+// region of the tile: wave w multiplies K quarters 2g and 2g + 1
+// (g = (w >> 1) & 1) of activation rows (BM/2) (w >> 2) .. and weight rows
+// (BN/2) (w & 1) .. of each stage.  After the last stage the partners swap
+// halves through the free ring: wave w keeps the int32 sums of activation
+// rows (BM/4) (w >> 1) .. + BM/4 - 1 (the half g of its region) and adds its
+// partner's (w ^ 2) sums of the same outputs - an exact integer addition, so
+// the results are gemm_pp's bits - which is the (BM/4) x (BN/2) layout of a
+// 4 x 2 wave grid, handed to the same epilogue.  At 128 x 128 this runs
+// eight waves (two per SIMD) on a tile that gemm_pp covers with four.
+template <int BM, int BN, int STA, int YDT>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(1, 4))) void
+gemm_pk(GemmArgs p) {
+    constexpr int BK = 128, NW = 8;
+    constexpr int FM = BM / 64, FN = BN / 64;         // fragments of a wave's region
+    constexpr int FH = FM / 2;                        // m-fragments of a half
+    constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW), L = LA + LB;
+    constexpr int SA = BM * BK, SB = BN * BK;
+    static_assert(FM >= 2 && FM % 2 == 0 && FN >= 1 && LA >= 1 && LB >= 1, "tile");
+    static_assert(STA >= 2 && STA * L < 64, "ring");
+    static_assert(NW * FN * FH * 4096 <= STA * (SA + SB), "exchange fits the ring");
+
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STA * (SA + SB)];
+    __shared__ __attribute__((aligned(16))) float sx[BM], sw[BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = (wave >> 1) & 1;                    // K half of each stage
+    const int mb = (wave >> 2) * (BM / 2), nb = (wave & 1) * (BN / 2);
+    int tile_m, tile_n;
+    tile_of(p, blockIdx.x, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int M = p.M, N = p.N, K = p.K;
+    TileScales<BM, BN> scl;
+    scl.load(p, m0, n0);
+
+    const int8_t *a_src[LA];
+    const int8_t *b_src[LB];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int row = (wave * LA + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gr = m0 + row < M ? m0 + row : M - 1;
+        a_src[j] = p.xq + (int64_t)gr * K + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int row = (wave * LB + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gr = n0 + row < N ? n0 + row : N - 1;
+        b_src[j] = p.wq + (int64_t)gr * K + c * 16;
+    }
+    const uint32_t waveu = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;
+    const uint32_t lds_a = lds0 + waveu * (LA * 1024u);
+    const uint32_t lds_b = lds0 + (uint32_t)(STA * SA) + waveu * (LB * 1024u);
+    const int nk = K / BK;
+    auto issue = [&](int s) {  // both operands of stage s (past the end: the last one)
+        const int sc = s < nk ? s : nk - 1;
+        const int8_t *ga[LA];
+        const int8_t *gb[LB];
+#pragma unroll
+        for (int j = 0; j < LA; ++j) ga[j] = a_src[j] + sc * BK;
+#pragma unroll
+        for (int j = 0; j < LB; ++j) gb[j] = b_src[j] + sc * BK;
+        lds_dma_run<LA, false>(ga, lds_a + (uint32_t)((s % STA) * SA));
+        lds_dma_run<LB, false>(gb, lds_b + (uint32_t)((s % STA) * SB));
+    };
+
+    const int fr = lane & 31, fh = lane >> 5;
+    const int fsw = swz(fr);
+    const int off0 = ((4 * g + fh) ^ fsw) << 4;       // quarter 2g
+    const int off1 = ((4 * g + 2 + fh) ^ fsw) << 4;   // quarter 2g + 1
+    auto read_frags = [&](int s, int off, int4v (&xf)[FM], int4v (&wf)[FN]) {
+        const int8_t *ab = smem + (s % STA) * SA + off;
+        const int8_t *bb = smem + STA * SA + (s % STA) * SB + off;
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+            xf[f] = *reinterpret_cast<const int4v *>(ab + (mb + f * 32 + fr) * BK);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            wf[f] = *reinterpret_cast<const int4v *>(bb + (nb + f * 32 + fr) * BK);
+    };
+
+    int16v acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+    auto mma = [&](const int4v (&xf)[FM], const int4v (&wf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Main loop: the quarter-2g fragments multiply while the quarter-2g+1
+    // ones load; after the stage barrier the next stage's quarter-2g loads
+    // and the stage's direct loads interleave with the quarter-2g+1 MFMAs.
+    constexpr int RQ = FM + FN, MQ = FM * FN;
+    static_assert(RQ <= MQ, "one read per MFMA slot");
+#pragma unroll
+    for (int s = 0; s < STA; ++s) issue(s);
+    wait_vmcnt<(STA - 1) * L>();
+    lds_barrier();
+    int4v xa[FM], wa[FN], xb[FM], wb[FN];
+    read_frags(0, off0, xa, wa);
+    for (int kt = 0; kt < nk; ++kt) {
+        read_frags(kt, off1, xb, wb);
+        mma(xa, wa);
+#pragma unroll
+        for (int r = 0; r < RQ; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        if constexpr (MQ > RQ) __builtin_amdgcn_sched_group_barrier(0x008, MQ - RQ, 0);
+        wait_vmcnt<(STA - 2) * L>();  // stage kt + 1 of both operands landed
+        lds_barrier();                // every wave has read stage kt: its slots are free
+        read_frags(kt + 1, off0, xa, wa);
+        issue(kt + STA);
+        mma(xb, wb);
+        sched_tail<MQ, RQ, L, 0>();
+    }
+    wait_vmcnt<0>();
+    scl.publish(sx, sw);
+    __syncthreads();  // ring free: every wave has read the last stage
+
+    // Swap halves with the partner through the ring: fragment (i, jj) of the
+    // half sent (m-fragment FH (1 - g) + jj) is written as 4 lane-major
+    // 16-byte rows at wave w's slot; the partner reads the same lane's
+    // values, so both sides keep the accumulator layout.  g is
+    // wave-uniform: one branch, static register indices.
+    constexpr int SLOT = FN * FH * 4 * 64;  // int4v per wave
+    int4v *const xs = reinterpret_cast<int4v *>(smem);
+    int4v *const mine = xs + wave * SLOT;
+    const int4v *const theirs = xs + (wave ^ 2) * SLOT;
+    int16v fin[FN][FH];
+    auto swap_halves = [&](auto g_c) {
+        constexpr int G = decltype(g_c)::value;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FH; ++jj)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int16v &a = acc[i][FH * (1 - G) + jj];
+                    mine[((i * FH + jj) * 4 + c) * 64 + lane] =
+                        int4v{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+                }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FH; ++jj)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int4v t = theirs[((i * FH + jj) * 4 + c) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        fin[i][jj][4 * c + e] = acc[i][FH * G + jj][4 * c + e] + t[e];
+                }
+    };
+    if (__builtin_amdgcn_readfirstlane(g)) swap_halves(std::integral_constant<int, 1>{});
+    else swap_halves(std::integral_constant<int, 0>{});
+    __syncthreads();  // exchange read: the epilogue reuses the ring
+    float side_unused[1][1][16];
+    epilogue_nt<BM, BN, 4, 2, YDT, false>(p, fin, smem, sx, sw, m0, n0, 0, side_unused, 0);
+}
+
 // ---------------------------------------------------------------- decode
 
 // Decode GEMM (M <= 32), bound by the weight stream.  A block owns 16*NF
@@ -1312,6 +1484,16 @@ static void launch_pipe_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     else gemm_pp<BM, BN, WM, WN, STA, STB, BF16, SIDE, F8><<<grid, block, 0, stream>>>(a);
 }
 
+template <int BM, int BN, int STA>
+static void launch_pk_t(GemmArgs &a, int y_dt, hipStream_t stream) {
+    const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    set_xcd_grid(a, tm, tn, BM, BN);
+    dim3 grid((unsigned)(tm * tn)), block(512);
+    if (y_dt == F32) gemm_pk<BM, BN, STA, F32><<<grid, block, 0, stream>>>(a);
+    else if (y_dt == F16) gemm_pk<BM, BN, STA, F16><<<grid, block, 0, stream>>>(a);
+    else gemm_pk<BM, BN, STA, BF16><<<grid, block, 0, stream>>>(a);
+}
+
 template <int NF, int FT, int U, int S, bool NT, bool F8 = false>
 static void launch_dec_t(GemmArgs &a, int y_dt, hipStream_t stream) {
     dim3 grid((unsigned)((a.N + 16 * NF - 1) / (16 * NF))), block(256);
@@ -1349,12 +1531,14 @@ static int pick_tile(int64_t M, int64_t N, int64_t K) {
         const double score = (double)tiles / (double)(rounds * slots) * cands[i].eff;
         if (score > best_score + 1e-9) { best_score = score; best = i; }
     }
-    // A short K with 256 x 128 tiles leaving at least half the CUs idle:
-    // 128 x 128 tiles give every CU a block (measured at 4096 x 1024 x 1024:
-    // 11.1 us against 12.3-12.8; at K = 3072 the larger tile stays ahead).
+    // 256 x 128 tiles leaving at least half the CUs idle: 128 x 128 tiles
+    // give every CU a block; at a short K four waves (measured at
+    // 4096 x 1024 x 1024: 11.1 us against 12.3-12.8), at a long K eight in
+    // K-split pairs (4096 x 1024 x 3072: 21.1 us against 23.5 with four
+    // waves and 25.8 on 256 x 128 tiles; at K = 1024 the pairs gain nothing).
     const int64_t t1 = ((M + 255) / 256) * ((N + 127) / 128);
     const int64_t t2 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (best == 1 && t1 <= 128 && t2 >= 256 && K <= 2048) return 2;
+    if (best == 1 && t1 <= 128 && t2 >= 256) return K <= 2048 ? 2 : 3;
     return best;
 }
 
@@ -1368,14 +1552,15 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
     a.xq = xq; a.wq = wq; a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.xs = x_scale; a.xs_per_row = per_row; a.ws = w_scale; a.y = y; a.acc_out = acc_out;
     const bool pipe = K % 128 == 0;
-    // force_tile 0 | 1 | 2 (the coverage entry points) overrides the choice.
-    const int tile = force_tile >= 0 && force_tile <= 2 ? force_tile : pick_tile(M, N, K);
+    // force_tile 0 | 1 | 2 | 3 (the coverage entry points) overrides the choice.
+    const int tile = force_tile >= 0 && force_tile <= 3 ? force_tile : pick_tile(M, N, K);
     if (side) {
         // With the side term 256 x 256 tiles would need the side sums next
         // to 128 accumulator registers: the 256-row choices take 256 x 128.
         a.x16 = side->x16; a.w16 = side->w16; a.idx = side->idx; a.count = side->count;
         a.xo = side->xo; a.wo = side->wo; a.side_cap = side->xo && side->wo ? side->cap : -1;
-        if (pipe && tile < 2) launch_pipe_t<256, 128, 4, 2, 3, 3, true>(a, y_dt, stream);
+        // (the K-split pairs have no side-term form: their choice keeps 256 x 128)
+        if (pipe && (tile < 2 || tile == 3)) launch_pipe_t<256, 128, 4, 2, 3, 3, true>(a, y_dt, stream);
         else if (pipe) launch_pipe_t<128, 128, 2, 2, 2, 2, true>(a, y_dt, stream);
         else launch_tile_t<128, 128, 2, 2, true>(a, y_dt, stream);
         return;
@@ -1398,13 +1583,14 @@ void launch_gemm(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64
         switch (tile) {
             case 0: launch_pipe_t<256, 256, 4, 2, 2, 2, false>(a, y_dt, stream); break;
             case 1: launch_pipe_t<256, 128, 4, 2, 3, 3, false>(a, y_dt, stream); break;
+            case 3: launch_pk_t<128, 128, 3>(a, y_dt, stream); break;
             default: launch_pipe_t<128, 128, 2, 2, 2, 2, false>(a, y_dt, stream); break;
         }
         return;
     }
-    switch (tile) {
+    switch (tile) {  // (3, the K-split pairs, needs K % 128 == 0: as 1 here)
         case 0: launch_tile_t<256, 256, 2, 2, false>(a, y_dt, stream); break;
-        case 1: launch_tile_t<256, 128, 2, 2, false>(a, y_dt, stream); break;
+        case 1: case 3: launch_tile_t<256, 128, 2, 2, false>(a, y_dt, stream); break;
         default: launch_tile_t<128, 128, 2, 2, false>(a, y_dt, stream); break;
     }
 }
@@ -1428,7 +1614,9 @@ void launch_gemm_fp8(const uint8_t *xq, const uint8_t *wq, int64_t M, int64_t N,
         else launch_dec_t<8, 2, 2, 2, true, true>(a, y_dt, stream);
         return;
     }
-    const int tile = force_tile >= 0 && force_tile <= 2 ? force_tile : pick_tile(M, N, K);
+    // (the K-split pairs, tile 3, are int8 only: their choice keeps 256 x 128)
+    const int t = force_tile >= 0 && force_tile <= 2 ? force_tile : pick_tile(M, N, K);
+    const int tile = t == 3 ? 1 : t;
     switch (tile) {
         case 0: launch_pipe_t<256, 256, 4, 2, 2, 2, false, true>(a, y_dt, stream); break;
         case 1: launch_pipe_t<256, 128, 4, 2, 3, 3, false, true>(a, y_dt, stream); break;

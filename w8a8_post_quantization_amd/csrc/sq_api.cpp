@@ -214,7 +214,7 @@ int sq_quantize_act(const void *x, int dt, int64_t M, int64_t K, const float *in
 int sq_gemm_i8_dequant_tile(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
                             const float *x_scale, int x_scale_per_row, const float *w_scale,
                             void *y, int y_dt, int32_t *acc_out, void *stream, int tile) {
-    if (tile < -1 || tile > 2) return SQ_ERR_ARG;
+    if (tile < -1 || tile > 3) return SQ_ERR_ARG;
     if (!valid_dt(y_dt)) return SQ_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 16 != 0)
         return SQ_ERR_SHAPE;
