@@ -131,6 +131,25 @@ def test_gemm_i8(torch, M):
     _twice(torch, run, f"int8 gemm M{M}")
 
 
+def test_gemm_i8_k_split_pairs(torch):
+    """The 128 x 128 K-split-pair kernel (forced): the partners' exchange of
+    int32 halves through LDS gives the same bits on every run."""
+    M, N, K = 1000, 1100, 4096
+    g = _gen(torch, 77)
+    xq = torch.randint(-127, 128, (M, K), generator=g, device="cuda", dtype=torch.int8)
+    wq = torch.randint(-127, 128, (N, K), generator=g, device="cuda", dtype=torch.int8)
+    xs = torch.rand(M, generator=g, device="cuda") * 0.01 + 1e-3
+    ws = torch.rand(N, generator=g, device="cuda") * 0.01 + 1e-3
+    log(f"determinism int8 gemm K-split pairs M{M} N{N} K{K}")
+
+    def run(fill):
+        y32 = _filled(torch, (M, N), torch.float32, fill)
+        y, acc = sq.gemm_i8_dequant(xq, wq, xs, ws, with_acc=True, out=y32, tile=3)
+        return [y, acc]
+
+    _twice(torch, run, "int8 gemm K-split pairs")
+
+
 @pytest.mark.parametrize("M", [1, 32, 2048])
 def test_gemm_fp8(torch, M):
     N, K = 8192, 7168
