@@ -515,6 +515,19 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most `later` stages of P loads each are in flight
+// (later <= L, or negative for none; vmcnt takes an immediate, hence the
+// unrolled choice).
+template <int L, int P>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (L == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= L) wait_vmcnt<L * P>();
+        else wait_stages<L - 1, P>(later);
+    }
+}
+
 // Workgroup barrier for the LDS ring only.  __syncthreads() carries a
 // release fence that waits for every outstanding global load (vmcnt(0)),
 // which would drain the in-flight stages; here each wave has already waited
@@ -862,18 +875,16 @@ gemm_pp(GemmArgs p) {
     const uint32_t lds_a = lds0 + waveu * (LA * 1024u);
     const uint32_t lds_b = lds0 + (uint32_t)(STA * SA) + waveu * (LB * 1024u);
     const int nk = K / BK;
-    auto issue_a = [&](int s) {  // activation stage s (past the end: the last one)
-        const int sc = s < nk ? s : nk - 1;
+    auto issue_a = [&](int s) {  // activation stage s < nk
         const int8_t *g[LA];
 #pragma unroll
-        for (int j = 0; j < LA; ++j) g[j] = a_src[j] + sc * BK;
+        for (int j = 0; j < LA; ++j) g[j] = a_src[j] + s * BK;
         lds_dma_run<LA, false>(g, lds_a + (uint32_t)((s % STA) * SA));
     };
-    auto issue_b = [&](int s) {
-        const int sc = s < nk ? s : nk - 1;
+    auto issue_b = [&](int s) {  // weight stage s < nk
         const int8_t *g[LB];
 #pragma unroll
-        for (int j = 0; j < LB; ++j) g[j] = b_src[j] + sc * BK;
+        for (int j = 0; j < LB; ++j) g[j] = b_src[j] + s * BK;
         lds_dma_run<LB, false>(g, lds_b + (uint32_t)((s % STB) * SB));
     };
 
@@ -931,15 +942,18 @@ gemm_pp(GemmArgs p) {
         };
 #pragma unroll
         for (int s = 0; s < STA; ++s) {
-            issue_a(s);
-            issue_b(s);
+            if (s < nk) {
+                issue_a(s);
+                issue_b(s);
+            }
         }
-        wait_vmcnt<(STA - 1) * L>();
+        wait_stages<STA - 1, L>((nk < STA ? nk : STA) - 1);  // stage 0 landed
         lds_barrier();
         int4v x0[FM], w0[FN], x1[FM], w1[FN], x2[FM], w2[FN], x3[FM], w3[FN];
         read_frags(0, 0, x0, w0);
         read_frags(0, 1, x1, w1);
-        for (int kt = 0; kt < nk; ++kt) {
+        int kt = 0;
+        for (; kt + STA < nk; ++kt) {
             read_frags(kt, 2, x2, w2);
             read_frags(kt, 3, x3, w3);
             mma8(x0, w0, x1, w1);
@@ -949,6 +963,16 @@ gemm_pp(GemmArgs p) {
             read_frags(kt + 1, 1, x1, w1);
             issue_a(kt + STA);
             issue_b(kt + STB);
+            mma8(x2, w2, x3, w3);
+        }
+        for (; kt < nk; ++kt) {  // nothing left to issue
+            read_frags(kt, 2, x2, w2);
+            read_frags(kt, 3, x3, w3);
+            mma8(x0, w0, x1, w1);
+            wait_stages<STA - 2, L>(nk - kt - 2);  // stage kt + 1 landed (if any)
+            lds_barrier();
+            read_frags(kt + 1, 0, x0, w0);  // past the last stage: never multiplied
+            read_frags(kt + 1, 1, x1, w1);
             mma8(x2, w2, x3, w3);
         }
         wait_vmcnt<0>();
@@ -962,10 +986,8 @@ gemm_pp(GemmArgs p) {
     // interleave: a wave issues in order, so a ds_read (or direct load)
     // queued behind an MFMA that waits for the matrix core cannot issue; the
     // sched_group_barrier sequences place one memory instruction after each
-    // MFMA.  Past the last stage, free ring slots are refilled with the last
-    // stage (never read), which keeps every iteration's load count - and so
-    // the vmcnt arithmetic - the same; all loads are drained before the
-    // epilogue.
+    // MFMA.  The last STA iterations (step_tail) issue no loads - there is no
+    // stage left - and wait for as many stages as are still in flight.
     constexpr int RQ = FM + FN;  // ds_read_b128 per quarter
     constexpr int MQ = FM * FN;  // MFMAs per quarter
     static_assert(RQ <= MQ, "one read per MFMA slot");
@@ -975,8 +997,10 @@ gemm_pp(GemmArgs p) {
                                                   (uint32_t)(uintptr_t)(lds_void_t *)sside);
 #pragma unroll
     for (int s = 0; s < STA; ++s) {
-        issue_a(s);
-        issue_b(s);
+        if (s < nk) {
+            issue_a(s);
+            issue_b(s);
+        }
     }
     // side columns summed in the main loop (kSideEarly at most, one per
     // stage; compact operands only)
@@ -984,14 +1008,39 @@ gemm_pp(GemmArgs p) {
     if constexpr (SIDE) {
         if (searly && scnt > 0 && scnt <= p.side_cap) {
             te = scnt < kSideEarly ? scnt : kSideEarly;
-            te = te < nk ? te : nk;
+            te = te < nk - STA ? te : nk - STA;  // stages that still issue loads
+            te = te > 0 ? te : 0;
         }
         t_from = te;
     }
-    wait_vmcnt<(STA - 1) * L>();
+    wait_stages<STA - 1, L>((nk < STA ? nk : STA) - 1);  // stage 0 landed
     lds_barrier();
     int4v xa[FM], wa[FN], xb[FM], wb[FN];
     read_frags(0, 0, xa, wa);
+    // A stage: quarters 1-3 read while 0-2 multiply, then the barrier, then
+    // the next stage's quarter 0 read (and, in step, the next loads issued)
+    // while quarter 3 multiplies.
+    auto step_tail = [&](int kt) {  // kt + STA >= nk: nothing left to issue
+        read_frags(kt, 1, xb, wb);
+        mma(xa, wa);
+        read_frags(kt, 2, xa, wa);
+        mma(xb, wb);
+        read_frags(kt, 3, xb, wb);
+        mma(xa, wa);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+#pragma unroll
+            for (int r = 0; r < RQ; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MQ - RQ, 0);
+        }
+        wait_stages<STA - 2, L>(nk - kt - 2);  // stage kt + 1 landed (if any)
+        lds_barrier();
+        read_frags(kt + 1, 0, xa, wa);  // past the last stage: never multiplied
+        mma(xb, wb);
+    };
     auto step = [&](int kt) {
         read_frags(kt, 1, xb, wb);
         mma(xa, wa);
@@ -1026,7 +1075,8 @@ gemm_pp(GemmArgs p) {
                                                          kt + 1, side);
         }
     }
-    for (; kt < nk; ++kt) step(kt);
+    for (; kt + STA < nk; ++kt) step(kt);
+    for (; kt < nk; ++kt) step_tail(kt);
     wait_vmcnt<0>();
     scl.publish(sx, sw);
     __syncthreads();  // steps visible; the side term may reuse the ring
@@ -1092,14 +1142,13 @@ gemm_pk(GemmArgs p) {
     const uint32_t lds_a = lds0 + waveu * (LA * 1024u);
     const uint32_t lds_b = lds0 + (uint32_t)(STA * SA) + waveu * (LB * 1024u);
     const int nk = K / BK;
-    auto issue = [&](int s) {  // both operands of stage s (past the end: the last one)
-        const int sc = s < nk ? s : nk - 1;
+    auto issue = [&](int s) {  // both operands of stage s < nk
         const int8_t *ga[LA];
         const int8_t *gb[LB];
 #pragma unroll
-        for (int j = 0; j < LA; ++j) ga[j] = a_src[j] + sc * BK;
+        for (int j = 0; j < LA; ++j) ga[j] = a_src[j] + s * BK;
 #pragma unroll
-        for (int j = 0; j < LB; ++j) gb[j] = b_src[j] + sc * BK;
+        for (int j = 0; j < LB; ++j) gb[j] = b_src[j] + s * BK;
         lds_dma_run<LA, false>(ga, lds_a + (uint32_t)((s % STA) * SA));
         lds_dma_run<LB, false>(gb, lds_b + (uint32_t)((s % STA) * SB));
     };
@@ -1137,15 +1186,18 @@ gemm_pk(GemmArgs p) {
     // Main loop: the quarter-2g fragments multiply while the quarter-2g+1
     // ones load; after the stage barrier the next stage's quarter-2g loads
     // and the stage's direct loads interleave with the quarter-2g+1 MFMAs.
+    // The last STA iterations issue no loads and wait for as many stages as
+    // are still in flight.
     constexpr int RQ = FM + FN, MQ = FM * FN;
     static_assert(RQ <= MQ, "one read per MFMA slot");
 #pragma unroll
-    for (int s = 0; s < STA; ++s) issue(s);
-    wait_vmcnt<(STA - 1) * L>();
+    for (int s = 0; s < STA; ++s)
+        if (s < nk) issue(s);
+    wait_stages<STA - 1, L>((nk < STA ? nk : STA) - 1);  // stage 0 landed
     lds_barrier();
     int4v xa[FM], wa[FN], xb[FM], wb[FN];
     read_frags(0, off0, xa, wa);
-    for (int kt = 0; kt < nk; ++kt) {
+    auto half = [&](int kt) {  // the quarter-2g MFMAs, quarter 2g + 1 read
         read_frags(kt, off1, xb, wb);
         mma(xa, wa);
 #pragma unroll
@@ -1154,12 +1206,23 @@ gemm_pk(GemmArgs p) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
         if constexpr (MQ > RQ) __builtin_amdgcn_sched_group_barrier(0x008, MQ - RQ, 0);
+    };
+    int kt = 0;
+    for (; kt + STA < nk; ++kt) {
+        half(kt);
         wait_vmcnt<(STA - 2) * L>();  // stage kt + 1 of both operands landed
         lds_barrier();                // every wave has read stage kt: its slots are free
         read_frags(kt + 1, off0, xa, wa);
         issue(kt + STA);
         mma(xb, wb);
         sched_tail<MQ, RQ, L, 0>();
+    }
+    for (; kt < nk; ++kt) {
+        half(kt);
+        wait_stages<STA - 2, L>(nk - kt - 2);  // stage kt + 1 landed (if any)
+        lds_barrier();
+        read_frags(kt + 1, off0, xa, wa);  // past the last stage: never multiplied
+        mma(xb, wb);
     }
     wait_vmcnt<0>();
     scl.publish(sx, sw);
@@ -1232,18 +1295,6 @@ gemm_pk(GemmArgs p) {
 template <int U>
 __device__ __forceinline__ int dec_swz(int r) {
     return (r / (4 / U)) & (4 * U - 1);
-}
-
-// Wait until at most `later` stages of P loads each are in flight
-// (later <= L; vmcnt takes an immediate, hence the unrolled choice).
-template <int L, int P>
-__device__ __forceinline__ void wait_stages(int later) {
-    if constexpr (L == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (later >= L) wait_vmcnt<L * P>();
-        else wait_stages<L - 1, P>(later);
-    }
 }
 
 template <int NF, int FT, int U, int S, int YDT, bool NT, bool F8 = false>
