@@ -716,6 +716,16 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
     static_assert(RB % 16 == 0 && WM * WN * 32 * RB <= (BM + BN) * 128 * 2, "slab");
     int8_t *slab = smem + wave * (32 * RB);
     const bool vec_y = ((N * (int)sizeof(T)) & 15) == 0 && ((uintptr_t)p.y & 15) == 0;
+    // The weight steps of this lane's columns, read once for every
+    // m-fragment (the slab's LDS traffic is what the epilogue waits on).
+    float4 dwv[SIDE ? 1 : FN][4];
+    if constexpr (!SIDE) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                dwv[i][g] = *reinterpret_cast<const float4 *>(sw + wn * WTN + i * 32 + 8 * g + 4 * fh);
+    }
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + j * 32 + fr;
@@ -726,7 +736,7 @@ __device__ __forceinline__ void epilogue_nt(const GemmArgs &p,
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int cl = i * 32 + 8 * g + 4 * fh;  // first of 4 columns in the wave tile
-                const float4 dw4 = *reinterpret_cast<const float4 *>(sw + wn * WTN + cl);
+                const float4 dw4 = dwv[SIDE ? 0 : i][g];
                 const float dwq[4] = {dw4.x, dw4.y, dw4.z, dw4.w};
                 T h[4];
 #pragma unroll
