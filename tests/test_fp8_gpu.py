@@ -188,7 +188,9 @@ YDT = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}
     (64, 256, 128, "f32", True, None), (300, 520, 1024, "f32", True, None),
     (1, 4096, 1024, "f16", False, None), (33, 1000, 256, "bf16", True, None),
     (257, 384, 2048, "f32", True, "0"), (513, 640, 1024, "f16", True, "1"),
-    (200, 300, 512, "f32", False, "2"), (8, 28672 // 8, 8192, "f16", True, None)])
+    (200, 300, 512, "f32", False, "2"), (8, 28672 // 8, 8192, "f16", True, None),
+    # fewer K stages than the ring holds (one or two of three)
+    (100, 300, 256, "bf16", True, "1"), (70, 130, 128, "f32", True, "1")])
 def test_gemm_fp8_parity(torch, M, N, K, ydt, per_row, tile):
     xq = _codes(M * 3 + K, (M, K), 2.0)
     wq = _codes(N * 5 + K, (N, K), 0.5)

@@ -145,6 +145,8 @@ GEMM_CASES = [
     # 4096 x 1024 x 3072, is the decoder-1024 down GEMM of test_configs_gpu)
     (260, 390, 2176, "f32", 1, "3"), (513, 257, 1024, "bf16", 0, "3"), (129, 200, 128, "f16", 1, "3"),
     (140, 150, 1040, "f16", 1, "3"),
+    # fewer K stages than the ring holds, or exactly as many
+    (200, 260, 256, "f16", 1, "1"), (300, 130, 384, "bf16", 1, "3"), (260, 300, 256, "f32", 1, "3"),
     # decode path (M <= 32): every rows-per-block choice (M <= 8, 16, 32),
     # K below one 128-byte stage, K not a multiple of the stage, ragged N
     (1, 1000, 8192, "f16", 1, None), (8, 333, 512, "f32", 1, None),
