@@ -137,3 +137,38 @@ def test_mixed_random_shape(torch, i):
     r = oracle.int8_mixed_matmul(X, wq_o, ws_o, W, c["thr"], y_dt=ydt)
     assert int(host(cnt, torch)[0]) == r["idx"].size
     assert_bits_equal(host(y, torch), r["y"], "y")
+
+
+N_TILED = 24
+
+
+def _tiled_case(i):
+    r = np.random.default_rng(9800 + i)
+    M = int(r.integers(33, 700))
+    N = int(r.integers(1, 800))
+    K = 128 * int(r.integers(1, 28)) if i % 3 else 16 * int(r.integers(1, 200))
+    return dict(M=M, N=N, K=K, tile=i % 4, ydt=("f32", "f16", "bf16")[int(r.integers(0, 3))],
+                per_row=bool(r.integers(0, 4)), seed=300 + i)
+
+
+@pytest.mark.parametrize("i", range(N_TILED))
+def test_gemm_random_shape_every_tile(torch, i):
+    """a5 on seeded random shapes with each tiled block shape forced in turn
+    (256 x 256, 256 x 128, 128 x 128 and the 128 x 128 K-split pairs), K with
+    and without whole 128-byte stages and with fewer stages than a ring holds:
+    int32 sums and narrowed outputs bit-exact against the oracle."""
+    c = _tiled_case(i)
+    log(f"tiled random case {i}: {c}")
+    r = np.random.default_rng(c["seed"])
+    M, N, K = c["M"], c["N"], c["K"]
+    xq = r.integers(-127, 128, (M, K), dtype=np.int8)
+    wq = r.integers(-127, 128, (N, K), dtype=np.int8)
+    xs = (r.random(M if c["per_row"] else 1) * 0.01 + 1e-3).astype(np.float32)
+    ws = (r.random(N) * 0.001 + 1e-5).astype(np.float32)
+    ydt = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[c["ydt"]]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[c["ydt"]]
+    y, acc = sq.gemm_i8_dequant(dev(xq, torch), dev(wq, torch), dev(xs, torch), dev(ws, torch),
+                                out_dtype=tdt, with_acc=True, tile=c["tile"])
+    y_o, acc_o = oracle.gemm_i8_dequant(xq, wq, xs, ws, y_dt=ydt, per_row=int(c["per_row"]))
+    assert_bits_equal(host(acc, torch), acc_o, "acc")
+    assert_bits_equal(host(y, torch), y_o, "y")
